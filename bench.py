@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""NF4 fused dequant-GEMV benchmark on one MI355X.
+
+A step is one decode pass over the linear layers of a model-shaped layer set:
+for every layer, every projection's packed NF4 weights are multiplied with its
+own activations (q, k, v, o, gate, up, down in order, one stream).  Weights are
+packed once before timing (the quantizer is offline work); the step moves the
+packed codes and scales, the bf16 activations and the fp32 outputs.
+
+Default workload: Llama-2-7B shapes, 32 layers of distinct seeded weights
+(3.44 GB packed, well beyond the 256 MB last-level cache), M = 1.
+
+Output: one JSON line.  value = effective HBM GB/s over the whole timed region
+(algorithmic bytes / wall time, sweeps replayed from a HIP graph captured before
+timing).  roofline = the dominant kernel's algorithmic GB/s from per-launch HIP
+events (launches queued behind a GPU sleep so that they run back to back).
+cpu_baseline = the CPU oracle on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import platform
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "NF4 GEMV effective HBM GB/s and % of peak at M=1; µs/layer-set (7B shapes)"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--set", default="llama2-7b",
+                    help="layer set: llama2-7b, llama2-13b, llama2-70b, llama3.1-8b-smallm, "
+                         "single-4096x4096")
+    ap.add_argument("--m", type=int, default=1, help="activation rows per product")
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = set's)")
+    ap.add_argument("--eager", action="store_true", help="time plain launches, no HIP graph")
+    ap.add_argument("--event-launches", type=int, default=64,
+                    help="launches per projection for the per-kernel event timing")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--out", default="", help="also append the JSON line to this file")
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(set_, M, seconds):
+    """Time the CPU oracle (as written, single thread) on a bounded sample: the
+    first 256 rows of each projection of layer 0, the same generated weights and
+    activations (drawn on the host generator: timing only, not parity)."""
+    import torch
+
+    import oracle
+    import workloads as wl
+    rows = 256
+    items = []
+    for proj, N, K in set_.projections:
+        n = min(rows, N)
+        W = wl.weights(n, K, set_.sigma, wl.seed_for(set_.name, 0, proj, "W"))
+        p, s, _ = oracle.quantize_pack(W.numpy())
+        x = wl.bf16_bits(wl.activations(M, K, wl.seed_for(set_.name, 0, proj, "x")))
+        items.append((p, s, x, wl.algorithmic_bytes(n, K, M)))
+    nbytes = 0
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for p, s, x, b in items:
+            oracle.gemm(p, s, x)
+            nbytes += b
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    del torch
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"layer 0 of {set_.name}, first {rows} rows of each of the "
+                      f"{len(set_.projections)} projections, M={M}, {reps} passes "
+                      f"in {dt:.1f} s (fp64 dequant-then-matvec, quantization untimed)",
+            "host": platform.processor() or platform.machine()}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}); this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import dequant_gemv_nf4_amd as nf4
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    set_ = wl.ALL_SETS[args.set]
+    M = args.m
+    L = args.layers or set_.layers
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device {props.name} {getattr(props, 'gcnArchName', '')}, set {set_.name}, "
+        f"layers {L}, M {M}")
+
+    # ---- setup: generate and pack every layer's weights on the GPU
+    t0 = time.perf_counter()
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    st_any = torch.zeros(1, dtype=torch.int32, device=dev)
+    items = []
+    for layer in range(L):
+        for proj, N, K in set_.projections:
+            W = wl.weights(N, K, set_.sigma, wl.seed_for(set_.name, layer, proj, "W"), dev)
+            codes, scales = nf4.empty_packed(N, K, dev)
+            nf4.nf4_pack(W, codes, scales, status)
+            st_any.bitwise_or_(status)
+            del W
+            X = wl.activations(M, K, wl.seed_for(set_.name, layer, proj, "x"), dev)
+            Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            items.append((proj, N, K, codes, scales, X, Y))
+    torch.cuda.synchronize()
+    if int(st_any.item()) != 0:
+        raise SystemExit(f"nf4_pack flagged groups: {int(st_any.item()):#x}")
+    packed_bytes = sum(c.numel() + 2 * s.numel() for _, _, _, c, s, _, _ in items)
+    step_bytes = sum(wl.algorithmic_bytes(N, K, M) for _, N, K, *_ in items)
+    log(f"packed {packed_bytes / 1e9:.2f} GB in {time.perf_counter() - t0:.1f} s; "
+        f"{step_bytes / 1e6:.2f} MB algorithmic per step")
+
+    def launch(it):
+        _, N, K, codes, scales, X, Y = it
+        if M == 1:
+            nf4.nf4_gemv(codes, scales, X, Y)
+        else:
+            nf4.nf4_gemm_smallm(codes, scales, X, Y)
+
+    def sweep():
+        for it in items:
+            launch(it)
+
+    # ---- warmup (eager), then capture one sweep into a HIP graph outside any timer
+    for _ in range(args.warmup):
+        sweep()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.eager:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            sweep()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            sweep()
+        torch.cuda.synchronize()
+        for _ in range(max(1, args.warmup)):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    # ---- timed region: K steps
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            sweep()
+    e1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_total = e0.elapsed_time(e1)
+    ms_per_step = ms_total / args.steps
+    value = step_bytes * args.steps / (ms_total / 1e3) / 1e9
+    log(f"{args.steps} steps: {ms_per_step * 1e3:.1f} us/step (host wall {t_wall * 1e3:.1f} ms), "
+        f"{value:.0f} GB/s")
+
+    # ---- per-kernel durations from HIP events (launches queued behind a GPU sleep)
+    per_proj = {}
+    order = [p for p, _, _ in set_.projections]
+    for proj in order:
+        its = [it for it in items if it[0] == proj]
+        nl = min(args.event_launches, 4 * len(its))
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(nl)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(2e7))  # keep the GPU busy while the launches queue up
+        for i in range(nl):
+            a, b = evs[i]
+            a.record()
+            launch(its[(i * 5 + 3) % len(its)])  # rotate through the layers
+            b.record()
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+        _, N, K, *_ = its[0]
+        per_proj[proj] = {"N": N, "K": K, "launches": nl, "us_mean": float(us.mean()),
+                          "us_median": float(np.median(us)), "us_p10": float(np.percentile(us, 10)),
+                          "us_p90": float(np.percentile(us, 90)),
+                          "bytes": wl.algorithmic_bytes(N, K, M)}
+        log(f"  {proj:5s} {N}x{K}: {per_proj[proj]['us_median']:.2f} us median, "
+            f"{per_proj[proj]['bytes'] / per_proj[proj]['us_median'] / 1e3:.0f} GB/s")
+
+    # dominant kernel: projections sharing the kernel instance with the largest share of
+    # per-step time; for M = 1 the instance is fixed by K (row units per lane)
+    groups = {}
+    for proj in order:
+        pp = per_proj[proj]
+        key = pp["K"]
+        n_in_step = sum(1 for it in items if it[0] == proj)
+        g = groups.setdefault(key, {"projs": [], "time": 0.0, "bytes": 0.0, "launch_us": [],
+                                    "launch_bytes": []})
+        g["projs"].append(proj)
+        g["time"] += pp["us_mean"] * n_in_step
+        g["bytes"] += pp["bytes"] * n_in_step
+        g["launch_us"].append(pp["us_mean"])
+        g["launch_bytes"].append(pp["bytes"])
+    dom_k = max(groups, key=lambda k: groups[k]["time"])
+    dom = groups[dom_k]
+    # per launch: mean algorithmic bytes / mean duration over the projections it serves
+    achieved = float(np.mean(dom["launch_bytes"]) / np.mean(dom["launch_us"]) / 1e3)
+    kernel_sum_us = sum(per_proj[p]["us_mean"] * sum(1 for it in items if it[0] == p)
+                        for p in order)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nf4-w/bf16-x/f16-dot/fp32-acc",
+        "data": "synthetic",
+        "config": {"workload": f"{set_.name} layer set, M={M}", "layers": L,
+                   "projections": [[p, N, K] for p, N, K in set_.projections],
+                   "m": M, "packed_gb": round(packed_bytes / 1e9, 3),
+                   "step_algorithmic_mb": round(step_bytes / 1e6, 3),
+                   "timing": "hip-graph replay" if graph is not None else "eager launches"},
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "us_per_layer_set": round(ms_per_step * 1e3 / L, 3),
+        "kernel_us_per_layer_set": round(kernel_sum_us / L, 3),
+        "per_projection": per_proj,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": f"gemv_valu_kernel (M={M}, K={dom_k})" if M < 8 else
+                               f"gemm_mfma_kernel (M={M}, K={dom_k})",
+                     "projections": dom["projs"],
+                     "bytes_per_launch": float(np.mean(dom["launch_bytes"])),
+                     "us_per_launch": round(float(np.mean(dom["launch_us"])), 3)},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline ...")
+        out["cpu_baseline"] = cpu_baseline(set_, M, args.cpu_seconds)
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

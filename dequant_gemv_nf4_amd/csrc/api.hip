@@ -1,0 +1,107 @@
+// api.hip -- the C ABI of libnf4 (declared in include/nf4.h): argument checks,
+// device check and kernel choice.  No allocation, no synchronization.
+#include <atomic>
+#include <cstring>
+
+#include "../../include/nf4.h"
+#include "nf4_device.h"
+#include "nf4_launch.h"
+
+namespace nf4 {
+bool valu_supported(int64_t N, int64_t K, int M);
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// per device: 0 = unknown, 1 = gfx950, 2 = other
+std::atomic<int> g_arch[kMaxDevices];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return NF4_ERANGE;
+  int a = g_arch[dev].load(std::memory_order_relaxed);
+  if (a == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return NF4_ERANGE;
+    a = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch[dev].store(a, std::memory_order_relaxed);
+  }
+  return a == 1 ? NF4_OK : NF4_EDEVICE;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_shape(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || K % NF4_GROUP != 0) return NF4_EINVAL;
+  if (K > NF4_MAX_K || N >= (int64_t(1) << 31)) return NF4_ERANGE;
+  return NF4_OK;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? NF4_OK : NF4_ELAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int nf4_pack(const float *W, int64_t N, int64_t K, uint8_t *codes, uint16_t *scales,
+             int32_t *dev_status, void *stream) {
+  if (!W || !codes || !scales) return NF4_EINVAL;
+  if (int r = check_shape(N, K)) return r;
+  if (!aligned(W, 4) || !aligned(codes, 4) || !aligned(scales, 2) ||
+      (dev_status && !aligned(dev_status, 4)))
+    return NF4_EALIGN;
+  if (int r = check_device()) return r;
+  return launched(nf4::launch_pack(W, N, K, codes, scales, dev_status, (hipStream_t)stream));
+}
+
+int nf4_unpack(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K, float *W_out,
+               void *stream) {
+  if (!codes || !scales || !W_out) return NF4_EINVAL;
+  if (int r = check_shape(N, K)) return r;
+  if (!aligned(codes, 4) || !aligned(scales, 2) || !aligned(W_out, 16)) return NF4_EALIGN;
+  if (int r = check_device()) return r;
+  return launched(nf4::launch_unpack(codes, scales, N, K, W_out, (hipStream_t)stream));
+}
+
+int nf4_gemm_smallm(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                    const uint16_t *X, int64_t M, float *Y, void *stream) {
+  if (!codes || !scales || !X || !Y) return NF4_EINVAL;
+  if (int r = check_shape(N, K)) return r;
+  if (M < 1 || M > NF4_MAX_M) return NF4_ERANGE;
+  if (!aligned(codes, 16) || !aligned(scales, 2) || !aligned(X, 16) || !aligned(Y, 4))
+    return NF4_EALIGN;
+  if (int r = check_device()) return r;
+  const int m = (int)M;
+  hipStream_t s = (hipStream_t)stream;
+  // M < 8 on the vector ALUs (decode shared across the M dot products); the
+  // batch tiles from 8 rows up, and the rare small-M shapes whose activations do
+  // not fit the VALU kernel's registers, on MFMA.
+  if (m < 8 && nf4::valu_supported(N, K, m))
+    return launched(nf4::launch_gemv_valu(codes, scales, N, K, X, m, Y, s));
+  return launched(nf4::launch_gemm_mfma(codes, scales, N, K, X, m, Y, s));
+}
+
+int nf4_gemv(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+             const uint16_t *x, float *y, void *stream) {
+  return nf4_gemm_smallm(codes, scales, N, K, x, 1, y, stream);
+}
+
+void nf4_codebook(float out[16]) {
+  if (!out) return;
+  for (int i = 0; i < 16; ++i) std::memcpy(&out[i], &nf4::kLevelBits[i], 4);
+}
+
+const char *nf4_strerror(int status) {
+  switch (status) {
+    case NF4_OK: return "ok";
+    case NF4_EINVAL: return "invalid argument (null pointer, N or K not positive, K % 64 != 0)";
+    case NF4_EALIGN: return "misaligned pointer";
+    case NF4_ERANGE: return "size out of range (M not in [1,32], K too large, N too large) or no device";
+    case NF4_EDEVICE: return "current device is not gfx950";
+    case NF4_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

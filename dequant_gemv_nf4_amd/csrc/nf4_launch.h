@@ -1,0 +1,22 @@
+// nf4_launch.h -- host-side launchers behind the C ABI (internal to libnf4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nf4 {
+
+hipError_t launch_pack(const float *W, int64_t N, int64_t K, uint8_t *codes, uint16_t *scales,
+                       int32_t *status, hipStream_t stream);
+hipError_t launch_unpack(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                         float *out, hipStream_t stream);
+
+// VALU product, 1 <= M <= 7 (the GEMV is M = 1).
+hipError_t launch_gemv_valu(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                            const uint16_t *X, int M, float *Y, hipStream_t stream);
+
+// MFMA product, 8 <= M <= 32.
+hipError_t launch_gemm_mfma(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                            const uint16_t *X, int M, float *Y, hipStream_t stream);
+
+}  // namespace nf4

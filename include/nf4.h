@@ -1,0 +1,125 @@
+/*
+ * nf4.h -- C ABI of libnf4: NF4 weight packing and the fused dequant
+ * matrix-vector / small-batch products for MI355X (gfx950).
+ *
+ * Problem statement (the sources):
+ *  - deep-fold README, "Method": weights are 4-bit NF4 codes in groups of 64
+ *    consecutive weights, one FP16 scale per group; packed codes and scales stay
+ *    in GPU memory and the linear kernels rebuild the values of the current tile
+ *    while multiplying, never writing a dense matrix back.  Decode is an N=1
+ *    GEMV; prefill runs the same product on chunks of at most 32 positions.
+ *  - Trapetum home page: the 4-bit weights are decoded inside the matmul, so the
+ *    full-precision matrix is never materialized.
+ *  - NF4 levels: QLoRA's 4-bit NormalFloat (named by the deep-fold README).
+ *  So every product computes  Y[m][n] = sum_k L[code(n,k)] * s(n, k/64) * X[m][k].
+ *
+ * Data layout (all row-major, contiguous, no padding or leading dimensions):
+ *  - W      fp32 [N][K]              input to nf4_pack only.
+ *  - codes  uint8 [N][K/2]           byte j of row n = code(n,2j) | code(n,2j+1) << 4
+ *                                    (low nibble = even k).
+ *  - scales uint16 [N][K/64]         IEEE binary16 bit patterns.
+ *  - x / X  uint16 bf16 bits [M][K]  (x is M = 1).
+ *  - y / Y  fp32 [M][N].
+ *  K must be a multiple of 64; every group lies inside one row.
+ *
+ * Ownership and execution:
+ *  - Every array argument is a device pointer owned by the caller.  The library
+ *    never frees or keeps a pointer, never writes its inputs, and keeps no
+ *    per-call state, so calls on different streams may run concurrently.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *    call only enqueues work on it and returns; there is no synchronization.
+ *  - Outputs are fully overwritten (no accumulation into y / Y).
+ *
+ * Errors: each call validates its arguments on the host before launching and
+ * returns one of the nf4_status codes; on any error nothing is enqueued and no
+ * memory is touched.  Asynchronous GPU faults surface on the stream as usual.
+ *
+ * Numerics: nf4_pack and nf4_unpack are exact (bit-for-bit defined below).
+ * nf4_gemv / nf4_gemm_smallm accumulate in fp32 with f16 products; per output
+ * element |Y - Y_exact| <= 2e-3 * sum_k |w~(n,k) X[m][k]| + 1e-5 for finite
+ * inputs whose products stay in range.  Results are deterministic: the same
+ * call on the same device gives the same bits.
+ */
+#ifndef NF4_H
+#define NF4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NF4_GROUP 64      /* weights per scale group, along K */
+#define NF4_MAX_M 32      /* largest activation batch of nf4_gemm_smallm */
+#define NF4_MAX_K 32768   /* largest supported K */
+
+enum nf4_status {
+  NF4_OK = 0,
+  NF4_EINVAL = -1,  /* null pointer, N <= 0, K <= 0, K % 64 != 0 */
+  NF4_EALIGN = -2,  /* codes / x / X not 16-byte aligned, scales / y not 2 / 4 */
+  NF4_ERANGE = -3,  /* M outside [1, 32], K > NF4_MAX_K, N >= 2^31, or no device */
+  NF4_EDEVICE = -4, /* current device is not gfx950 */
+  NF4_ELAUNCH = -5  /* the HIP launch itself failed */
+};
+
+/* bits OR-ed into *dev_status by nf4_pack */
+#define NF4_PACK_NONFINITE 1      /* a group holds NaN or +-inf */
+#define NF4_PACK_SCALE_OVERFLOW 2 /* group absmax rounds to fp16 infinity (>= 65520) */
+
+/*
+ * nf4_pack -- quantize fp32 W [N][K] to NF4 codes and fp16 group scales.
+ * Source: deep-fold README, "Method" (group of 64, NF4 codes, one FP16 scale).
+ * Per group of 64 along K:
+ *   s = binary16(max |w|), round to nearest even;
+ *   code(w) = number of i in 0..14 with w > (L[i] + L[i+1]) / 2 * s, evaluated
+ *             exactly (fp64) -- the nearest level L[c]*s to w, ties to the lower
+ *             code; if s == 0 every code is 7 (the zero level).
+ * A group holding a non-finite value, or whose absmax rounds to fp16 infinity,
+ * is written as scale 0 and codes 7, and the matching NF4_PACK_* bit is OR-ed
+ * into *dev_status (device int32).  dev_status may be NULL; if given, the call
+ * first clears it to 0 on the stream.
+ * Alignment: W 4 bytes, codes 4 bytes, scales 2 bytes.
+ */
+int nf4_pack(const float *W, int64_t N, int64_t K, uint8_t *codes, uint16_t *scales,
+             int32_t *dev_status, void *stream);
+
+/*
+ * nf4_unpack -- dequantize to fp32 W_out [N][K]:  W_out = fp32(L[c] * s), one
+ * correctly rounded fp32 multiply.  Exists to check the format bit for bit; the
+ * products never call it.  Source: deep-fold README, "Method".
+ * Alignment: codes 4 bytes, scales 2 bytes, W_out 16 bytes.
+ */
+int nf4_unpack(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+               float *W_out, void *stream);
+
+/*
+ * nf4_gemv -- y[n] = sum_k L[code(n,k)] * s(n,k/64) * x[k]  (M = 1, decode).
+ * Source: deep-fold README, "Method" (N=1 GEMV of resident decode); Trapetum
+ * overview, "The bandwidth law" (the cost is reading the packed weights).
+ * The dense matrix is never formed: codes are expanded in registers.
+ * Alignment: codes 16 bytes, scales 2, x 16, y 4.
+ */
+int nf4_gemv(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+             const uint16_t *x, float *y, void *stream);
+
+/*
+ * nf4_gemm_smallm -- Y[m][n] = sum_k L[code(n,k)] * s(n,k/64) * X[m][k] for
+ * 1 <= M <= 32 (prefill chunks, speculative verification batches).
+ * Source: deep-fold README, "Method" (prompt chunks of up to 32 positions on a
+ * tensor-core NF4 GEMM).  M = 1 is the GEMV; M >= 8 runs on MFMA.
+ * Alignment: codes 16 bytes, scales 2, X 16, Y 4.
+ */
+int nf4_gemm_smallm(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                    const uint16_t *X, int64_t M, float *Y, void *stream);
+
+/* The 16 NF4 levels L[0..15] (fp32) this library decodes with.  Host only. */
+void nf4_codebook(float out[16]);
+
+/* Static string for an nf4_status code.  Host only. */
+const char *nf4_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NF4_H */

@@ -1,0 +1,99 @@
+"""Host-side checks of libnf4.so that need no GPU: it loads, exports every symbol
+include/nf4.h declares, its codebook equals the oracle's bit for bit, and its
+argument validation returns the documented status codes before touching a
+device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nf4.h")
+LIB = os.path.join(ROOT, "dequant_gemv_nf4_amd", "libnf4.so")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nf4_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libnf4.so is not built (run __graft_entry__.build())")
+    L = ctypes.CDLL(LIB)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    L.nf4_pack.argtypes = [vp, i64, i64, vp, vp, vp, vp]
+    L.nf4_unpack.argtypes = [vp, vp, i64, i64, vp, vp]
+    L.nf4_gemv.argtypes = [vp, vp, i64, i64, vp, vp, vp]
+    L.nf4_gemm_smallm.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp]
+    L.nf4_strerror.restype = ctypes.c_char_p
+    return L
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for required in ("nf4_pack", "nf4_unpack", "nf4_gemv", "nf4_gemm_smallm", "nf4_codebook",
+                     "nf4_strerror"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_codebook_bitwise_equals_oracle(lib):
+    out = (ctypes.c_float * 16)()
+    lib.nf4_codebook(out)
+    got = np.frombuffer(bytes(out), dtype=np.float32)
+    _, l32 = oracle.codebook()
+    assert np.array_equal(got.view(np.uint32), l32.view(np.uint32))
+
+
+P = ctypes.c_void_p(0x100000)      # fake, 16-byte aligned; never dereferenced on these paths
+P_ODD = ctypes.c_void_p(0x100002)  # 2-byte aligned only
+NULL = ctypes.c_void_p(0)
+EINVAL, EALIGN, ERANGE = -1, -2, -3
+
+
+@pytest.mark.parametrize("N,K,expect", [(0, 64, EINVAL), (-1, 64, EINVAL), (4, 0, EINVAL),
+                                        (4, 100, EINVAL), (4, 65, EINVAL), (4, 32768 + 64, ERANGE),
+                                        (2 ** 31, 64, ERANGE)])
+def test_shape_validation(lib, N, K, expect):
+    assert lib.nf4_gemv(P, P, N, K, P, P, NULL) == expect
+    assert lib.nf4_gemm_smallm(P, P, N, K, P, 4, P, NULL) == expect
+    assert lib.nf4_pack(P, N, K, P, P, NULL, NULL) == expect
+    assert lib.nf4_unpack(P, P, N, K, P, NULL) == expect
+
+
+def test_null_pointers(lib):
+    assert lib.nf4_gemv(NULL, P, 4, 64, P, P, NULL) == EINVAL
+    assert lib.nf4_gemv(P, NULL, 4, 64, P, P, NULL) == EINVAL
+    assert lib.nf4_gemv(P, P, 4, 64, NULL, P, NULL) == EINVAL
+    assert lib.nf4_gemv(P, P, 4, 64, P, NULL, NULL) == EINVAL
+    assert lib.nf4_pack(NULL, 4, 64, P, P, NULL, NULL) == EINVAL
+    assert lib.nf4_unpack(P, P, 4, 64, NULL, NULL) == EINVAL
+
+
+@pytest.mark.parametrize("M", [0, -3, 33, 1000])
+def test_m_range(lib, M):
+    assert lib.nf4_gemm_smallm(P, P, 4, 64, P, M, P, NULL) == ERANGE
+
+
+def test_alignment(lib):
+    assert lib.nf4_gemv(P_ODD, P, 4, 64, P, P, NULL) == EALIGN   # codes need 16 B
+    assert lib.nf4_gemv(P, P, 4, 64, P_ODD, P, NULL) == EALIGN   # x needs 16 B
+    assert lib.nf4_gemv(P, P, 4, 64, P, P_ODD, NULL) == EALIGN   # y needs 4 B
+    assert lib.nf4_gemv(P, ctypes.c_void_p(0x100001), 4, 64, P, P, NULL) == EALIGN
+    assert lib.nf4_unpack(P, P, 4, 64, P_ODD, NULL) == EALIGN
+
+
+def test_strerror(lib):
+    for code in (0, -1, -2, -3, -4, -5, 7):
+        assert isinstance(lib.nf4_strerror(code), bytes)

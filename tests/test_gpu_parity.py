@@ -1,0 +1,256 @@
+"""GPU parity: libnf4 (through its C ABI, via the ctypes binding) against the CPU
+oracle on the same seeded inputs.
+
+Bars: nf4_pack codes and scales and nf4_unpack values bit-exact; products within
+|y - y_ref| <= 2e-3 * sum_k |w~ x| + 1e-5 per element (y_ref, the bound and the
+oracle's own codes all come from oracle/ on host copies of the generated
+inputs, never from the GPU).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def nf4():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import dequant_gemv_nf4_amd as m
+    m._lib._load()  # fail loudly if the library is missing
+    return m
+
+
+def _host_pack(W):
+    packed, scales, st = oracle.quantize_pack(W.detach().cpu().numpy())
+    return packed, scales, st
+
+
+def _check_product(Y_gpu, Y_ref, A, what):
+    Y = Y_gpu.detach().cpu().numpy().astype(np.float64).reshape(Y_ref.shape)
+    ok = oracle.within_tolerance(Y, Y_ref, A)
+    if not ok.all():
+        idx = np.argwhere(~ok)[:5]
+        det = [(tuple(i), Y[tuple(i)], Y_ref[tuple(i)], A[tuple(i)]) for i in idx]
+        pytest.fail(f"{what}: {int((~ok).sum())} of {ok.size} outside tolerance, e.g. {det}")
+
+
+def _pack_gpu(nf4, W):
+    N, K = W.shape
+    codes, scales = nf4.empty_packed(N, K, W.device)
+    st = torch.full((1,), -7, dtype=torch.int32, device=W.device)
+    nf4.nf4_pack(W, codes, scales, st)
+    torch.cuda.synchronize()
+    return codes, scales, int(st.item())
+
+
+def _u16(t):
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+# ------------------------------------------------------------------ packing
+@pytest.mark.parametrize("N,K,sigma", [(1, 64, 0.02), (3, 128, 1.0), (17, 192, 0.02),
+                                       (64, 4096, 0.02), (5, 11008, 0.015), (2, 32768, 3.0)])
+def test_pack_bit_exact(nf4, N, K, sigma):
+    W = wl.weights(N, K, sigma, seed=1000 + N * 7 + K, device=DEV)
+    codes, scales, st = _pack_gpu(nf4, W)
+    ref_p, ref_s, ref_st = _host_pack(W)
+    assert st == ref_st == 0
+    assert np.array_equal(codes.cpu().numpy(), ref_p)
+    assert np.array_equal(_u16(scales), ref_s)
+
+
+def test_pack_adversarial_values(nf4):
+    """Decision boundaries and their fp32 neighbours, zero and tiny groups, huge and
+    subnormal-scale groups; flagged groups (NaN, inf, overflow) and the status word."""
+    _, l32 = oracle.codebook()
+    mids = (l32[:-1].astype(np.float64) + l32[1:].astype(np.float64)) / 2
+    row = []
+    for m in mids:
+        f = np.float32(m)
+        row += [f, np.nextafter(f, np.float32(2)), np.nextafter(f, np.float32(-2)), -f]
+    row += [0.0, -0.0, 1.0, -1.0]
+    row = np.array(row, np.float32)
+    W = np.zeros((6, 128), np.float32)
+    W[0, :len(row[:64])] = row[:64]
+    W[0, 63] = 1.0
+    W[0, 64:64 + len(row[64:])] = row[64:]
+    W[0, 127] = -1.0
+    W[1, :64] = 0.0                                  # zero group -> s = 0, codes 7
+    W[1, 64:] = np.float32(2.0 ** -26)               # rounds to s = 0
+    rng = np.random.default_rng(99)
+    W[2, :64] = (rng.standard_normal(64) * 3e-6).astype(np.float32)   # subnormal fp16 scale
+    W[2, 64:] = (rng.standard_normal(64) * 2e4).astype(np.float32)    # large, still finite
+    W[3, :64] = np.float32(65519.0)                  # largest absmax that fits
+    W[3, 64:] = (rng.standard_normal(64)).astype(np.float32)
+    W[4, :] = 0.5
+    W[4, 5] = np.nan                                 # non-finite -> flagged group
+    W[5, :64] = 0.25
+    W[5, 64:] = 0.5
+    W[5, 100] = 70000.0                              # overflow -> flagged group
+    Wg = torch.from_numpy(W).to(DEV)
+    codes, scales, st = _pack_gpu(nf4, Wg)
+    ref_p, ref_s, ref_st = oracle.quantize_pack(W)
+    assert st == ref_st == (oracle.STATUS_NONFINITE | oracle.STATUS_SCALE_OVERFLOW)
+    assert np.array_equal(codes.cpu().numpy(), ref_p)
+    assert np.array_equal(_u16(scales), ref_s)
+    # without a status word the call still packs identically
+    codes2, scales2 = nf4.empty_packed(6, 128, DEV)
+    nf4.nf4_pack(Wg, codes2, scales2, None)
+    torch.cuda.synchronize()
+    assert torch.equal(codes2, codes) and torch.equal(scales2, scales)
+
+
+@pytest.mark.parametrize("N,K", [(7, 64), (33, 320), (128, 4096)])
+def test_unpack_bit_exact(nf4, N, K):
+    W = wl.weights(N, K, 0.02, seed=77 + N, device=DEV)
+    ref_p, ref_s, _ = _host_pack(W)
+    codes = torch.from_numpy(ref_p).to(DEV)
+    scales = torch.from_numpy(ref_s.view(np.int16)).to(DEV)
+    Wt = nf4.unpack(codes, scales, K)
+    torch.cuda.synchronize()
+    ref = oracle.dequant_f32(ref_p, ref_s)
+    assert np.array_equal(Wt.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+# ------------------------------------------------------------------ products
+def _product_case(nf4, M, N, K, sigma=0.02, seed=0, via_gemv=None):
+    W = wl.weights(N, K, sigma, seed=seed * 1009 + N * 31 + K, device=DEV)
+    X = wl.activations(M, K, seed=seed * 2003 + M * 17 + K, device=DEV)
+    codes, scales, st = _pack_gpu(nf4, W)
+    ref_p, ref_s, _ = _host_pack(W)
+    assert np.array_equal(codes.cpu().numpy(), ref_p)
+    if via_gemv or (via_gemv is None and M == 1):
+        Y = nf4.gemv(codes, scales, X[0])
+    else:
+        Y = nf4.gemm(codes, scales, X)
+    torch.cuda.synchronize()
+    Yr, A = oracle.gemm(ref_p, ref_s, wl.bf16_bits(X))
+    _check_product(Y, Yr, A, f"M={M} N={N} K={K}")
+    return codes, scales, X, Y
+
+
+@pytest.mark.parametrize("N", [1, 15, 16, 17, 300, 1024])
+@pytest.mark.parametrize("K", [64, 128, 4096, 5120, 11008])
+def test_gemv_shape_sweep(nf4, N, K):
+    _product_case(nf4, 1, N, K)
+
+
+def test_gemv_single_4096(nf4):
+    """The single 4096 x 4096 GEMV workload, every output checked."""
+    _product_case(nf4, 1, 4096, 4096, seed=1)
+
+
+def test_gemv_large_k_and_ragged(nf4):
+    _product_case(nf4, 1, 33, 32768)
+    _product_case(nf4, 1, 129, 28672)
+    _product_case(nf4, 1, 4099, 64)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 7, 8, 9, 16, 17, 31, 32])
+def test_gemm_smallm_m_sweep(nf4, M):
+    _product_case(nf4, M, 272, 1024, seed=M)
+
+
+@pytest.mark.parametrize("M,N,K", [(4, 33, 14336), (8, 100, 4096), (32, 48, 14336),
+                                   (5, 20, 20480), (8, 17, 64), (32, 1, 128), (16, 4111, 192)])
+def test_gemm_smallm_shapes(nf4, M, N, K):
+    _product_case(nf4, M, N, K, seed=3)
+
+
+def test_product_exact_identities(nf4):
+    N, K = 300, 1024
+    W = wl.weights(N, K, 0.02, seed=5, device=DEV)
+    codes, scales, _ = _pack_gpu(nf4, W)
+    for M in (1, 4, 8, 32):
+        X = wl.activations(M, K, seed=6, device=DEV)
+        Y = nf4.gemm(codes, scales, X)
+        # zero activations -> exactly zero
+        Z = nf4.gemm(codes, scales, torch.zeros_like(X))
+        # power-of-two scaling commutes bitwise
+        Y4 = nf4.gemm(codes, scales, (X.float() * 4.0).to(torch.bfloat16))
+        Yq = nf4.gemm(codes, scales, (X.float() * 0.25).to(torch.bfloat16))
+        # the same call twice -> the same bits
+        Y2 = nf4.gemm(codes, scales, X)
+        torch.cuda.synchronize()
+        assert torch.all(Z == 0), M
+        assert torch.equal(Y4, Y * 4.0), M
+        assert torch.equal(Yq, Y * 0.25), M
+        assert torch.equal(Y2, Y), M
+    # every code the zero level -> y = 0
+    zc = torch.full_like(codes, 0x77)
+    X = wl.activations(8, K, seed=7, device=DEV)
+    assert torch.all(nf4.gemm(zc, scales, X) == 0)
+    assert torch.all(nf4.gemv(zc, scales, X[0]) == 0)
+
+
+def test_activation_range_extremes(nf4):
+    """Activations far outside the f16 range (huge, tiny, mixed) stay within tolerance."""
+    N, K = 64, 2048
+    W = wl.weights(N, K, 0.02, seed=8, device=DEV)
+    codes, scales, _ = _pack_gpu(nf4, W)
+    ref_p, ref_s, _ = _host_pack(W)
+    for M in (1, 3, 8, 32):
+        X = wl.activations(M, K, seed=9, device=DEV).float()
+        X[0] *= 1e30
+        if M > 1:
+            X[1] *= 1e-30
+        if M > 2:
+            X[2, ::2] *= 1e6
+        Xb = X.to(torch.bfloat16)
+        Y = nf4.gemm(codes, scales, Xb)
+        torch.cuda.synchronize()
+        Yr, A = oracle.gemm(ref_p, ref_s, wl.bf16_bits(Xb))
+        _check_product(Y, Yr, A, f"range M={M}")
+
+
+# ------------------------------------------------------------------ full sizes, sampled rows
+def _sampled_rows(N, count, seed):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(N, size=min(count, N), replace=False).tolist())
+    rows |= {0, N - 1}
+    return np.array(sorted(rows), np.int64)
+
+
+def _full_size_case(nf4, set_, proj, N, K, M):
+    W = wl.weights(N, K, set_.sigma, wl.seed_for(set_.name, 0, proj, "W"), device=DEV)
+    X = wl.activations(M, K, wl.seed_for(set_.name, 0, proj, "x"), device=DEV)
+    codes, scales, st = _pack_gpu(nf4, W)
+    assert st == 0
+    Y = nf4.gemv(codes, scales, X[0]) if M == 1 else nf4.gemm(codes, scales, X)
+    torch.cuda.synchronize()
+    rows = _sampled_rows(N, 48, N + K + M)
+    Wr = W[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    ref_p, ref_s, _ = oracle.quantize_pack(Wr)
+    r = torch.from_numpy(rows).to(DEV)
+    assert np.array_equal(codes[r].cpu().numpy(), ref_p), f"{set_.name}/{proj} codes"
+    assert np.array_equal(_u16(scales[r]), ref_s), f"{set_.name}/{proj} scales"
+    Yr, A = oracle.gemm(ref_p, ref_s, wl.bf16_bits(X))
+    _check_product(Y.reshape(M, N)[:, r], Yr, A, f"{set_.name}/{proj} M={M}")
+    del W
+
+
+@pytest.mark.parametrize("set_", [wl.SET_7B, wl.SET_13B, wl.SET_70B], ids=lambda s: s.name)
+def test_full_size_layer_shapes_m1(nf4, set_):
+    seen = set()
+    for proj, N, K in set_.projections:
+        if (N, K) in seen:
+            continue
+        seen.add((N, K))
+        _full_size_case(nf4, set_, proj, N, K, 1)
+
+
+@pytest.mark.parametrize("M", [4, 8, 32])
+def test_full_size_smallm_8b(nf4, M):
+    seen = set()
+    for proj, N, K in wl.SET_8B_SMALLM.projections:
+        if (N, K) in seen:
+            continue
+        seen.add((N, K))
+        _full_size_case(nf4, wl.SET_8B_SMALLM, proj, N, K, M)
