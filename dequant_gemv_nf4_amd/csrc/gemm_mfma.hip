@@ -48,9 +48,16 @@ __global__ void __launch_bounds__(kThreads)
   constexpr int KS = 8 / T;        // K-slices per row tile
   constexpr int MP = 16 * MT;      // staged activation rows
   constexpr int GPW = 8 / KS;      // groups per chunk handled by one wave
-  __shared__ uint32_t lut[kLutWords];
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][MP][kXStride];
-  __shared__ float fx[2][MP];
+  // one LDS block carved by hand: the decode table first, at offset 0, so that its
+  // byte addresses need no base added before each read
+  constexpr int kXsWords = 2 * MP * kXStride / 2;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[kLutWords + kXsWords + 2 * MP];
+  uint32_t *const lut = lds;
+  typedef uint16_t XRow[kXStride];
+  XRow *const xs0 = reinterpret_cast<XRow *>(lds + kLutWords);  // [2][MP] rows
+  float *const fx0 = reinterpret_cast<float *>(lds + kLutWords + kXsWords);  // [2][MP]
+  auto xs = [&](int buf, int row) -> uint16_t * { return xs0[buf * MP + row]; };
+  auto fx = [&](int buf, int row) -> float & { return fx0[buf * MP + row]; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -123,10 +130,10 @@ __global__ void __launch_bounds__(kThreads)
         o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
                ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
       }
-      *reinterpret_cast<uint4 *>(&xs[buf][srow][spart * EPT + 8 * v]) =
+      *reinterpret_cast<uint4 *>(&xs(buf, srow)[spart * EPT + 8 * v]) =
           make_uint4(o[0], o[1], o[2], o[3]);
     }
-    if (spart == 0) fx[buf][srow] = ldexpf(1.0f, -sh);
+    if (spart == 0) fx(buf, srow) = ldexpf(1.0f, -sh);
   };
 
   uint2 wcur[GPW];
@@ -172,7 +179,7 @@ __global__ void __launch_bounds__(kThreads)
         const float sc = f16_bits_to_f32(scur[j]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const uint16_t *xrow = &xs[buf][mt * 16 + col][q * 64 + lg * 16];
+          const uint16_t *xrow = &xs(buf, mt * 16 + col)[q * 64 + lg * 16];
           const uint4 a0 = *reinterpret_cast<const uint4 *>(xrow);
           const uint4 a1 = *reinterpret_cast<const uint4 *>(xrow + 8);
           f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a0), as_f16x8(b[0]),
@@ -187,7 +194,7 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[mt][r] = fmaf(cacc[mt][r], fx[buf][mt * 16 + lg * 4 + r], acc[mt][r]);
+      for (int r = 0; r < 4; ++r) acc[mt][r] = fmaf(cacc[mt][r], fx(buf, mt * 16 + lg * 4 + r), acc[mt][r]);
     if (more) {
       stage_x(buf ^ 1, xraw);
 #pragma unroll
@@ -200,7 +207,7 @@ __global__ void __launch_bounds__(kThreads)
   }
 
   // ---- sum the KS slice partials of each tile in slice order; reuse xs as scratch
-  float *red = reinterpret_cast<float *>(&xs[0][0][0]);  // needs 8 * 64 * 4 * MT floats
+  float *red = reinterpret_cast<float *>(xs0);  // needs 8 * 64 * 4 * MT floats
   if (KS > 1) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)

@@ -16,8 +16,7 @@ constexpr uint32_t kLevelBits[16] = {
     0xbdba7869u, 0x00000000u, 0x3da2fb01u, 0x3e24cadfu, 0x3e7c04dau, 0x3ead0336u,
     0x3ee1a4b5u, 0x3f1007a9u, 0x3f3913b0u, 0x3f800000u};
 
-// Level c as fp32, through a chain of selects (no memory access: the decode
-// tables are built from this once per workgroup).
+// Level c as fp32, through a chain of selects (no memory access).
 __device__ __forceinline__ float level_f32(uint32_t c) {
   uint32_t r = kLevelBits[0];
 #pragma unroll
@@ -25,11 +24,18 @@ __device__ __forceinline__ float level_f32(uint32_t c) {
   return __uint_as_float(r);
 }
 
-// f16 bit pattern of level c (round to nearest even, the hardware conversion).
-__device__ __forceinline__ uint32_t level_f16_bits(uint32_t c) {
-  _Float16 h = (_Float16)level_f32(c);
-  return (uint32_t)__builtin_bit_cast(uint16_t, h);
+// f16 bit patterns of the levels, rounded to nearest even at compile time.
+struct LevelF16 {
+  uint32_t v[16];
+};
+constexpr LevelF16 make_level_f16() {
+  LevelF16 r{};
+  for (int i = 0; i < 16; ++i)
+    r.v[i] = (uint32_t)__builtin_bit_cast(uint16_t,
+                                          (_Float16)__builtin_bit_cast(float, kLevelBits[i]));
+  return r;
 }
+constexpr LevelF16 kLevelF16 = make_level_f16();
 
 // ---------------------------------------------------------------------------
 // Byte decode table in LDS.
@@ -42,13 +48,32 @@ __device__ __forceinline__ uint32_t level_f16_bits(uint32_t c) {
 // ---------------------------------------------------------------------------
 constexpr int kLutWords = 256 * 64;  // 64 KiB
 
+// Wave w writes the entries whose high nibble h satisfies h % nwaves == w: for
+// one h that is 16 entries x 64 copies = 256 uint4 stores, 4 per lane.  Store
+// (h, j, lane) covers entry 16h + 4j + lane/16, so the high level is a constant
+// of the unrolled loop and the low level a 4-way choice fixed per lane.
 __device__ __forceinline__ void build_byte_lut(uint32_t *lut, int tid, int nthreads) {
-  // 16384 words written as 4096 uint4 stores of a splatted entry; an entry's
-  // 64 copies take 16 consecutive stores, so store index q -> entry q / 16.
-  for (int q = tid; q < kLutWords / 4; q += nthreads) {
-    uint32_t b = (uint32_t)q >> 4;
-    uint32_t e = level_f16_bits(b & 15u) | (level_f16_bits(b >> 4) << 16);
-    reinterpret_cast<uint4 *>(lut)[q] = make_uint4(e, e, e, e);
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nwaves = nthreads >> 6;
+  const uint32_t sub = (uint32_t)lane >> 4;
+  uint32_t lo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t a = kLevelF16.v[4 * j + 0], b = kLevelF16.v[4 * j + 1];
+    const uint32_t c = kLevelF16.v[4 * j + 2], d = kLevelF16.v[4 * j + 3];
+    lo[j] = sub == 0 ? a : (sub == 1 ? b : (sub == 2 ? c : d));
+  }
+  uint4 *L4 = reinterpret_cast<uint4 *>(lut);
+#pragma unroll
+  for (int h = 0; h < 16; ++h) {
+    if (h % nwaves == wave) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t e = lo[j] | (kLevelF16.v[h] << 16);
+        L4[h * 256 + j * 64 + lane] = make_uint4(e, e, e, e);
+      }
+    }
   }
 }
 
@@ -65,11 +90,6 @@ __device__ __forceinline__ uint32_t lds_load_u32(const uint32_t *base, uint32_t 
   return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(base) + byte_addr);
 }
 
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
-__device__ __forceinline__ uint32_t as_u32(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
-
 // bf16 bits -> fp32 (exact)
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -79,11 +99,51 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-// Sum over the 64 lanes of a wave, same bits in every lane; fixed order.
+// Power-of-two shift that puts the largest of a set of bf16 magnitudes just
+// under 2^15 (mx = the largest |x| as bf16 bits without sign).
+__device__ __forceinline__ int f16_range_shift(uint32_t mx) {
+  int e = 0;
+  (void)frexpf(__uint_as_float(mx << 16), &e);  // max < 2^e
+  return 15 - e;
+}
+
+// two bf16 (one word) -> two f16 scaled by 2^sh (one word), nearest even
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w, int sh) {
+  const _Float16 lo = (_Float16)ldexpf(bf16_lo(w), sh);
+  const _Float16 hi = (_Float16)ldexpf(bf16_hi(w), sh);
+  return (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+
+// largest |value| of the two bf16 in a word, as sign-less bf16 bits
+__device__ __forceinline__ uint32_t bf16x2_absmax_bits(uint32_t w) {
+  const uint32_t a = w & 0x7fff7fffu;
+  return max(a & 0xffffu, a >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// Wave reductions with DPP row operations plus lane reads: no LDS traffic.
+// Every lane of a row of 16 ends with the row's sum after four steps (xor 1,
+// xor 2, half-row mirror, row mirror -- each pairs lanes symmetrically, so all
+// 16 lanes hold identical bits); the four row sums are then added in row order.
+// ---------------------------------------------------------------------------
+template <int ctrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl,
+                                                               0xf, 0xf, false));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141>(v);  // row_half_mirror
+  v += dpp_f32<0x140>(v);  // row_mirror
+  const int b = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
