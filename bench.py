@@ -12,8 +12,8 @@ Default workload: Llama-2-7B shapes, 32 layers of distinct seeded weights
 
 Output: one JSON line.  value = effective HBM GB/s over the whole timed region
 (algorithmic bytes / wall time, sweeps replayed from a HIP graph captured before
-timing).  roofline = the dominant kernel's algorithmic GB/s from per-launch HIP
-events (launches queued behind a GPU sleep so that they run back to back).
+timing).  roofline = the dominant kernel's algorithmic GB/s from HIP events around
+graph replays of that kernel's launches (per-launch duration = elapsed / launches).
 cpu_baseline = the CPU oracle on a bounded sample of the same workload.
 """
 import argparse
@@ -49,7 +49,26 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out", default="", help="also append the JSON line to this file")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (5 times): the reference "
+                         "kernel whose FETCH_SIZE / WRITE_SIZE counters calibrate the HBM "
+                         "byte counters, then exit")
     return ap.parse_args()
+
+
+def recorded_traffic(key):
+    """HBM bytes per launch measured with rocprofv3 counters for the dominant kernel,
+    if the kernel sources still hash to what was profiled (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        entry = json.load(open(path))[key]
+        src = b"".join(open(os.path.join(ROOT, f), "rb").read() for f in entry["sources"])
+        if hashlib.sha256(src).hexdigest() == entry["source_sha256"]:
+            return entry["bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        pass
+    return None
 
 
 def log(*a):
@@ -109,6 +128,16 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 5}))
+        return
     set_ = wl.ALL_SETS[args.set]
     M = args.m
     L = args.layers or set_.layers
@@ -190,30 +219,43 @@ def main():
     log(f"{args.steps} steps: {ms_per_step * 1e3:.1f} us/step (host wall {t_wall * 1e3:.1f} ms), "
         f"{value:.0f} GB/s")
 
-    # ---- per-kernel durations from HIP events (launches queued behind a GPU sleep)
+    # ---- per-kernel durations: a HIP graph of R launches of one projection
+    # (rotating through the layers) replayed between two HIP events on the stream
+    # the kernels run on; duration = elapsed / R (graph nodes run back to back)
     per_proj = {}
     order = [p for p, _, _ in set_.projections]
     for proj in order:
         its = [it for it in items if it[0] == proj]
-        nl = min(args.event_launches, 4 * len(its))
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(nl)]
+        nl = max(1, min(args.event_launches, 4 * len(its)))
+        g = torch.cuda.CUDAGraph()
+        s2 = torch.cuda.Stream()
+        s2.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s2):
+            launch(its[0])
+        torch.cuda.current_stream().wait_stream(s2)
         torch.cuda.synchronize()
-        torch.cuda._sleep(int(2e7))  # keep the GPU busy while the launches queue up
-        for i in range(nl):
-            a, b = evs[i]
+        with torch.cuda.graph(g):
+            for i in range(nl):
+                launch(its[(i * 5 + 3) % len(its)])
+        g.replay()
+        torch.cuda.synchronize()
+        us = []
+        for _ in range(5):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
             a.record()
-            launch(its[(i * 5 + 3) % len(its)])  # rotate through the layers
+            g.replay()
             b.record()
-        torch.cuda.synchronize()
-        us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+            torch.cuda.synchronize()
+            us.append(a.elapsed_time(b) * 1e3 / nl)
+        us = np.array(us)
         _, N, K, *_ = its[0]
-        per_proj[proj] = {"N": N, "K": K, "launches": nl, "us_mean": float(us.mean()),
-                          "us_median": float(np.median(us)), "us_p10": float(np.percentile(us, 10)),
-                          "us_p90": float(np.percentile(us, 90)),
-                          "bytes": wl.algorithmic_bytes(N, K, M)}
-        log(f"  {proj:5s} {N}x{K}: {per_proj[proj]['us_median']:.2f} us median, "
-            f"{per_proj[proj]['bytes'] / per_proj[proj]['us_median'] / 1e3:.0f} GB/s")
+        per_proj[proj] = {"N": N, "K": K, "launches": nl * len(us), "us_mean": float(us.mean()),
+                          "us_median": float(np.median(us)), "us_min": float(us.min()),
+                          "us_max": float(us.max()), "bytes": wl.algorithmic_bytes(N, K, M)}
+        log(f"  {proj:5s} {N}x{K}: {per_proj[proj]['us_mean']:.2f} us per launch, "
+            f"{per_proj[proj]['bytes'] / per_proj[proj]['us_mean'] / 1e3:.0f} GB/s")
+        del g
 
     # dominant kernel: projections sharing the kernel instance with the largest share of
     # per-step time; for M = 1 the instance is fixed by K (row units per lane)
@@ -259,7 +301,9 @@ def main():
         "kernel_us_per_layer_set": round(kernel_sum_us / L, 3),
         "per_projection": per_proj,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": (recorded_traffic("gemv_valu_kernel M=1 llama2-7b q,k,v,o,gate,up")
+                                 if (M == 1 and set_.name == "llama2-7b") else None),
                      "kernel": f"gemv_valu_kernel (M={M}, K={dom_k})" if M < 8 else
                                f"gemm_mfma_kernel (M={M}, K={dom_k})",
                      "projections": dom["projs"],
