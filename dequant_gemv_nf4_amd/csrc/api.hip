@@ -35,6 +35,7 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int check_shape(int64_t N, int64_t K) {
   if (N <= 0 || K <= 0 || K % NF4_GROUP != 0) return NF4_EINVAL;
   if (K > NF4_MAX_K || N >= (int64_t(1) << 31)) return NF4_ERANGE;
+  if (N * (K / 2) >= (int64_t(1) << 31)) return NF4_ERANGE;  // codes of one matrix < 2 GiB
   return NF4_OK;
 }
 

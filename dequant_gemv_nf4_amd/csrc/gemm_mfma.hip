@@ -1,275 +1,307 @@
-// gemm_mfma.hip -- fused NF4 dequant product for activation batches of 8..32 rows
-// on the matrix cores (gfx950, v_mfma_f32_16x16x32_f16).
+// gemm_mfma.hip -- fused NF4 dequant product for activation batches of up to 32
+// rows on the matrix cores (gfx950, v_mfma_f32_16x16x32_bf16).
 //
 // Computes Y[m][n] = sum_k L[code(n,k)] * s(n,k/64) * X[m][k].  Source:
-// deep-fold README, "Method": prefill runs the NF4 product on prompt chunks of
-// up to 32 positions, rebuilding weights into matrix-core register fragments.
+// deep-fold README, "Method": prefill runs the NF4 product on prompt chunks of up
+// to 32 positions, rebuilding weights into matrix-core register fragments.
 //
-// MFMA mapping (D = A.B + C, 16 x 16 x 32):
-//   A = activations, 16 rows m x 32 k, in f16;
+// MFMA mapping (D = A.B + C, 16 x 16 x 32, bf16 operands, fp32 accumulate):
+//   A = activations, 16 rows m x 32 k: the bf16 inputs as they are, loaded from
+//       memory straight into the fragment (no conversion, no staging);
 //   B = decoded weights, 32 k x 16 columns n (one weight row per column);
 //   D = Y tile: lane l holds Y[4*(l/16) + r][n0 + l%16], r = 0..3.
-// Lane l supplies k-slots 8*(l/16) .. +7 of both A and B.  Within one scale
-// group (64 k) the slots of lane-group g in step h are k = 16g + 8h + e, so a
-// lane's 16 weights of a group are one 8-byte load and its 16 activations are 32
-// contiguous bytes.  Both steps of a group land in a scratch tile D_g, which is
-// scaled by that weight row's group scale in fp32 (lane-local: the scale belongs
-// to the lane's own column) and added to a chunk accumulator.  No weight is
-// rounded together with its scale.
+// Lane l supplies k-slots 8*(l/16) .. +7 of both A and B.  In scale group q,
+// step h (0, 1), the slots of lane-group g are k = 64q + 16g + 8h + e, so a
+// lane's 16 weights of a group are one 8-byte load and its 16 activations are
+// 32 contiguous bytes.
 //
-// Activations: the block stages X[:, chunk] (KC = 512 k) in LDS as f16, each row
-// m multiplied by a power of two so that its largest |x| in the chunk sits just
-// under 2^15 (exact conversion from bf16 down to 2^-29 of that maximum); the
-// chunk accumulator is multiplied back by that power of two when the chunk ends.
-// Staging of chunk c+1 overlaps the products of chunk c (double buffer).
+// A level in bf16 alone would be off by up to 2^-9 of itself, so each level is
+// split into hi = bf16(L) and lo = bf16(L - hi) (|L - hi - lo| < 2^-17 |L|) and
+// each step runs two MFMAs, A.B_hi and A.B_lo, into one group tile.  With exact
+// activations every product is exact in fp32.  The group tile is scaled by the
+// lane's own column scale in fp32 and added to the accumulator: no weight is
+// ever rounded together with its scale.
 //
-// Work split: 8 waves per block = T row tiles (16 rows each) x KS K-slices; the
-// slices of a tile take interleaved groups of each chunk.  Their partial tiles
-// are summed in LDS in slice order at the end: deterministic, no atomics.
-// Decode: same bank-replicated byte table and v_perm addressing as the GEMV.
+// Decode: a byte table in LDS; entry b holds the (hi pair, lo pair) of b's two
+// nibbles, 8 bytes, in 32 copies 8 bytes apart so that lane l reads copy l % 32
+// and no two lanes of a half-wave share a bank; the address is one v_perm_b32 of
+// the code word.  64 KiB.
+//
+// Work: a workgroup of 8 waves (one per CU) owns TB consecutive 16-column tiles.
+// Wave w takes scale groups w, w+8, w+16, ... of all TB tiles, so one activation
+// fragment serves TB tiles and the eight waves read neighbouring 32-byte pieces
+// of each weight row together.  A register ring holds the loads of the next D
+// groups; every load is unconditional (past-the-end groups and tiles re-read a
+// valid address), so waits are exact.  The 8 partial tiles are summed in LDS in
+// wave order: deterministic, no atomics.
+#include <utility>
+
 #include "nf4_device.h"
 #include "nf4_launch.h"
 
 namespace nf4 {
 
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kKC = 512;                  // k per staged chunk (8 groups)
-constexpr int kXStride = kKC + 8;         // f16 elements per staged row (16 B pad)
-constexpr int kThreads = 512;             // 8 waves
+constexpr int kThreads = 512;  // 8 waves
+constexpr int kWaves = kThreads / 64;
 
-__device__ __forceinline__ f16x8_t as_f16x8(uint4 v) { return __builtin_bit_cast(f16x8_t, v); }
+// ---------------------------------------------------------------------------
+// bf16 hi / lo split of the levels, at compile time (round to nearest even).
+// ---------------------------------------------------------------------------
+constexpr uint32_t bf16_rne_bits(uint32_t f) { return (f + 0x7fffu + ((f >> 16) & 1u)) >> 16; }
 
-template <int MT, int T>
+struct LevelSplit {
+  uint32_t hi[16];
+  uint32_t lo[16];
+};
+constexpr LevelSplit make_level_split() {
+  LevelSplit r{};
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t h = bf16_rne_bits(kLevelBits[i]);
+    const float rest =
+        __builtin_bit_cast(float, kLevelBits[i]) - __builtin_bit_cast(float, h << 16);
+    r.hi[i] = h;
+    r.lo[i] = bf16_rne_bits(__builtin_bit_cast(uint32_t, rest));
+  }
+  return r;
+}
+constexpr LevelSplit kSplit = make_level_split();
+
+// Entry b (b = 16 h + j, j = low nibble = even k) at byte 256 b + 8 c, copy c:
+//   word 0 = hi[j] | hi[h] << 16,  word 1 = lo[j] | lo[h] << 16.
+// Wave w writes the 16 entries of each high nibble h with h % 8 == w: 4096
+// contiguous bytes = 256 uint4 (two copies each), 4 per lane; store (i, lane)
+// covers entry 16h + 4i + lane/16, so the high level is a constant of the
+// unrolled loop and the low level a 4-way choice fixed per lane.
+__device__ __forceinline__ void build_split_lut(uint32_t *lut, int lane, int wave) {
+  // the 4-way choice as a shift of four packed 16-bit constants (a select chain
+  // would be turned into a table in memory)
+  const uint32_t sh = 16u * ((uint32_t)lane >> 4);
+  uint32_t lhi[4], llo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    constexpr auto pack4 = [](const uint32_t *v) {
+      return (uint64_t)v[0] | (uint64_t)v[1] << 16 | (uint64_t)v[2] << 32 | (uint64_t)v[3] << 48;
+    };
+    lhi[i] = (uint32_t)(pack4(&kSplit.hi[4 * i]) >> sh) & 0xffffu;
+    llo[i] = (uint32_t)(pack4(&kSplit.lo[4 * i]) >> sh) & 0xffffu;
+  }
+  uint4 *L4 = reinterpret_cast<uint4 *>(lut);
+#pragma unroll
+  for (int h = 0; h < 16; ++h) {
+    if (h % kWaves == wave) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t eh = lhi[i] | (kSplit.hi[h] << 16);
+        const uint32_t el = llo[i] | (kSplit.lo[h] << 16);
+        L4[h * 256 + i * 64 + lane] = make_uint4(eh, el, eh, el);
+      }
+    }
+  }
+}
+
+// v_perm_b32 selector: (byte j of the code word) << 8 | (low byte of laneoff)
+template <int j>
+__device__ __forceinline__ uint32_t split_addr(uint32_t codeword, uint32_t laneoff) {
+  constexpr uint32_t sel = 0x0c0c0000u | ((4u + j) << 8);
+  return __builtin_amdgcn_perm(codeword, laneoff, sel);
+}
+
+__device__ __forceinline__ u32x2_t lds_load_u64(const uint32_t *base, uint32_t byte_addr) {
+  return *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const char *>(base) + byte_addr);
+}
+
+__device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+template <int d>
+using Slot = std::integral_constant<int, d>;
+
+// f(Slot<0>{}), f(Slot<1>{}), ... f(Slot<D-1>{}): ring slots as compile-time
+// indices, so the ring stays in registers
+template <typename F, int... d>
+__device__ __forceinline__ void for_slots(F &&f, std::integer_sequence<int, d...>) {
+  (f(Slot<d>{}), ...);
+}
+
+// MT = 16-row activation tiles (1 for M <= 16, else 2); TB = column tiles per
+// workgroup; D = groups in flight per wave.
+template <int MT, int TB, int D>
 __global__ void __launch_bounds__(kThreads)
     gemm_mfma_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
                      const uint16_t *__restrict__ X, float *__restrict__ Y, int N, int K, int M) {
-  constexpr int KS = 8 / T;        // K-slices per row tile
-  constexpr int MP = 16 * MT;      // staged activation rows
-  constexpr int GPW = 8 / KS;      // groups per chunk handled by one wave
-  // one LDS block carved by hand: the decode table first, at offset 0, so that its
-  // byte addresses need no base added before each read
-  constexpr int kXsWords = 2 * MP * kXStride / 2;
-  __shared__ __attribute__((aligned(16))) uint32_t lds[kLutWords + kXsWords + 2 * MP];
-  uint32_t *const lut = lds;
-  typedef uint16_t XRow[kXStride];
-  XRow *const xs0 = reinterpret_cast<XRow *>(lds + kLutWords);  // [2][MP] rows
-  float *const fx0 = reinterpret_cast<float *>(lds + kLutWords + kXsWords);  // [2][MP]
-  auto xs = [&](int buf, int row) -> uint16_t * { return xs0[buf * MP + row]; };
-  auto fx = [&](int buf, int row) -> float & { return fx0[buf * MP + row]; };
+  // one LDS block: the decode table while the groups run, then the partial tiles
+  constexpr int kRedWords = kWaves * TB * MT * 4 * 64;
+  constexpr int kLdsWords = kRedWords > kLutWords ? kRedWords : kLutWords;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsWords];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int tile = wave / KS;
-  const int ks = wave % KS;
-  const int lg = lane >> 4;        // lane group: k-slot block
-  const int col = lane & 15;       // weight row within the tile / activation row within A
-  const int n = (blockIdx.x * T + tile) * 16 + col;
-  const bool nvalid = n < N;
-  const int64_t row_bytes = K >> 1;
-  const int64_t row_groups = K >> 6;
-  const int nchunks = (K + kKC - 1) / kKC;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, lg = lane >> 4;
+  const int NG = K >> 6;
+  const int NT = (N + 15) >> 4;
+  const int t0 = blockIdx.x * TB;
+  const int nsteps = wave < NG ? (NG - 1 - wave) / kWaves + 1 : 0;
 
-  // ---- weights: this wave's groups of a chunk, one 8-byte load per lane per group
-  auto load_w = [&](int c, uint2 *w, uint32_t *s) {
+  // per-lane offsets: weight row of column n in each tile (tiles past the end
+  // re-read the first tile, columns past N re-read row N-1) and activation row
+  uint32_t coff[TB], soff[TB];
 #pragma unroll
-    for (int j = 0; j < GPW; ++j) {
-      const int q = ks + j * KS;                 // group within the chunk
-      const int gk = c * (kKC / 64) + q;         // group index along K
-      if (nvalid && gk < row_groups) {
-        w[j] = *reinterpret_cast<const uint2 *>(codes + (int64_t)n * row_bytes + gk * 32 + lg * 8);
-        s[j] = scales[(int64_t)n * row_groups + gk];
-      } else {
-        w[j] = make_uint2(0, 0);
-        s[j] = 0;
-      }
+  for (int j = 0; j < TB; ++j) {
+    const int t = (t0 + j < NT) ? t0 + j : t0;
+    const uint32_t n = (uint32_t)min(16 * t + col, N - 1);
+    coff[j] = n * (uint32_t)(K >> 1) + 8u * lg;
+    soff[j] = n * (uint32_t)NG;
+  }
+  uint32_t xoff[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) xoff[mt] = (uint32_t)min(16 * mt + col, M - 1) * K + 16u * lg;
+
+  u32x2_t rc[D][TB];
+  uint32_t rs[D][TB];
+  u32x4_t ra[D][MT][2];
+
+  auto load = [&](auto slot, int i) __attribute__((always_inline)) {
+    constexpr int d = decltype(slot)::value;
+    const uint32_t q = (uint32_t)min(wave + kWaves * i, NG - 1);
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      rc[d][j] = *reinterpret_cast<const u32x2_t *>(codes + coff[j] + 32u * q);
+      rs[d][j] = scales[soff[j] + q];
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const u32x4_t *p = reinterpret_cast<const u32x4_t *>(X + xoff[mt] + 64u * q);
+      ra[d][mt][0] = p[0];
+      ra[d][mt][1] = p[1];
     }
   };
 
-  // ---- activations: 16 threads per staged row; 32 bf16 per thread
-  constexpr int TPR = kThreads / MP;             // threads per row (16 or 32)
-  constexpr int EPT = kKC / TPR;                 // elements per thread (32 or 16)
-  const int srow = tid / TPR;
-  const int spart = tid % TPR;
-  auto load_x = [&](int c, uint4 *raw) {
-    const int k0 = c * kKC + spart * EPT;
+  f32x4_t acc[TB][MT];
 #pragma unroll
-    for (int v = 0; v < EPT / 8; ++v) {
-      if (srow < M && k0 + 8 * v < K)
-        raw[v] = *reinterpret_cast<const uint4 *>(X + (int64_t)srow * K + k0 + 8 * v);
-      else
-        raw[v] = make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto stage_x = [&](int buf, const uint4 *raw) {
-    uint32_t mx = 0;
+  for (int j = 0; j < TB; ++j)
 #pragma unroll
-    for (int v = 0; v < EPT / 8; ++v) {
-      const uint32_t w4[4] = {raw[v].x, raw[v].y, raw[v].z, raw[v].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t a = w4[i] & 0x7fff7fffu;
-        mx = max(mx, max(a & 0xffffu, a >> 16));
-      }
-    }
-#pragma unroll
-    for (int off = 1; off < TPR; off <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
-    int e = 0;
-    (void)frexpf(__uint_as_float(mx << 16), &e);
-    const int sh = 15 - e;
-#pragma unroll
-    for (int v = 0; v < EPT / 8; ++v) {
-      const uint32_t w4[4] = {raw[v].x, raw[v].y, raw[v].z, raw[v].w};
-      uint32_t o[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        _Float16 lo = (_Float16)ldexpf(bf16_lo(w4[i]), sh);
-        _Float16 hi = (_Float16)ldexpf(bf16_hi(w4[i]), sh);
-        o[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-      }
-      *reinterpret_cast<uint4 *>(&xs(buf, srow)[spart * EPT + 8 * v]) =
-          make_uint4(o[0], o[1], o[2], o[3]);
-    }
-    if (spart == 0) fx(buf, srow) = ldexpf(1.0f, -sh);
-  };
+    for (int mt = 0; mt < MT; ++mt) acc[j][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint2 wcur[GPW];
-  uint32_t scur[GPW];
-  load_w(0, wcur, scur);
-  uint4 xraw[EPT / 8];
-  load_x(0, xraw);
-  build_byte_lut(lut, tid, kThreads);
-  stage_x(0, xraw);
-  __syncthreads();
-
-  const uint32_t laneoff = (uint32_t)lane * 4u;
-  f32x4_t acc[MT];
+  const uint32_t laneoff = 8u * (lane & 31);
+  auto compute = [&](auto slot) __attribute__((always_inline)) {
+    constexpr int d = decltype(slot)::value;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
-    const bool more = c + 1 < nchunks;
-    uint2 wnxt[GPW];
-    uint32_t snxt[GPW];
-    if (more) {
-      load_w(c + 1, wnxt, snxt);
-      load_x(c + 1, xraw);
-    }
-    f32x4_t cacc[MT];
+    for (int j = 0; j < TB; ++j) {
+      f32x4_t g[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) cacc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < GPW; ++j) {
-      const int q = ks + j * KS;
-      if (c * (kKC / 64) + q < row_groups) {     // uniform across the wave
-        // decode the lane's 16 weights into two B fragments (steps h = 0, 1)
-        uint4 b[2];
-        const uint32_t wd[2] = {wcur[j].x, wcur[j].y};
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          b[h].x = lds_load_u32(lut, lut_addr<0>(wd[h], laneoff));
-          b[h].y = lds_load_u32(lut, lut_addr<1>(wd[h], laneoff));
-          b[h].z = lds_load_u32(lut, lut_addr<2>(wd[h], laneoff));
-          b[h].w = lds_load_u32(lut, lut_addr<3>(wd[h], laneoff));
-        }
-        const float sc = f16_bits_to_f32(scur[j]);
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t w = rc[d][j][h];
+        u32x4_t bh, bl;
+        u32x2_t e;
+        e = lds_load_u64(lds, split_addr<0>(w, laneoff)); bh[0] = e[0]; bl[0] = e[1];
+        e = lds_load_u64(lds, split_addr<1>(w, laneoff)); bh[1] = e[0]; bl[1] = e[1];
+        e = lds_load_u64(lds, split_addr<2>(w, laneoff)); bh[2] = e[0]; bl[2] = e[1];
+        e = lds_load_u64(lds, split_addr<3>(w, laneoff)); bh[3] = e[0]; bl[3] = e[1];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const uint16_t *xrow = &xs(buf, mt * 16 + col)[q * 64 + lg * 16];
-          const uint4 a0 = *reinterpret_cast<const uint4 *>(xrow);
-          const uint4 a1 = *reinterpret_cast<const uint4 *>(xrow + 8);
-          f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a0), as_f16x8(b[0]),
-                                                            f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a1), as_f16x8(b[1]), d, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) cacc[mt][r] = fmaf(d[r], sc, cacc[mt][r]);
+          g[mt] = mfma_bf16(ra[d][mt][h], bh, h == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : g[mt]);
+          g[mt] = mfma_bf16(ra[d][mt][h], bl, g[mt]);
         }
       }
-    }
-    // undo the chunk's activation scaling: rows m = 16 mt + 4 lg + r
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[mt][r] = fmaf(cacc[mt][r], fx(buf, mt * 16 + lg * 4 + r), acc[mt][r]);
-    if (more) {
-      stage_x(buf ^ 1, xraw);
-#pragma unroll
-      for (int j = 0; j < GPW; ++j) {
-        wcur[j] = wnxt[j];
-        scur[j] = snxt[j];
-      }
-    }
-    __syncthreads();
-  }
-
-  // ---- sum the KS slice partials of each tile in slice order; reuse xs as scratch
-  float *red = reinterpret_cast<float *>(xs0);  // needs 8 * 64 * 4 * MT floats
-  if (KS > 1) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) red[((wave * MT + mt) * 4 + r) * 64 + lane] = acc[mt][r];
-    __syncthreads();
-    if (ks == 0) {
+      const float s = f16_bits_to_f32(rs[d][j]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float s = 0.0f;
-          for (int j = 0; j < KS; ++j) s += red[(((wave + j) * MT + mt) * 4 + r) * 64 + lane];
-          acc[mt][r] = s;
-        }
+        for (int r = 0; r < 4; ++r) acc[j][mt][r] = fmaf(g[mt][r], s, acc[j][mt][r]);
     }
+  };
+
+  // prologue: the first D groups in flight while the table is built
+  for_slots([&](auto slot) __attribute__((always_inline)) { load(slot, decltype(slot)::value); },
+            std::make_integer_sequence<int, D>{});
+  build_split_lut(lds, lane, wave);
+  __syncthreads();
+
+  for (int base = 0; base < nsteps; base += D) {
+    for_slots(
+        [&](auto slot) __attribute__((always_inline)) {
+          constexpr int d = decltype(slot)::value;
+          if (base + d < nsteps) compute(slot);
+          load(slot, base + d + D);
+        },
+        std::make_integer_sequence<int, D>{});
   }
-  if (ks == 0 && nvalid) {
+
+  // partial tiles of the 8 waves, summed in wave order
+  __syncthreads();  // the table is no longer read
+  float *red = reinterpret_cast<float *>(lds);
+#pragma unroll
+  for (int j = 0; j < TB; ++j)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = mt * 16 + lg * 4 + r;
-        if (m < M) Y[(int64_t)m * N + n] = acc[mt][r];
-      }
+      for (int r = 0; r < 4; ++r)
+        red[(((wave * TB + j) * MT + mt) * 4 + r) * 64 + lane] = acc[j][mt][r];
+  __syncthreads();
+  constexpr int kOut = TB * MT * 256;  // outputs per workgroup
+  for (int o = tid; o < kOut; o += kThreads) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) s += red[w * kOut + o];
+    const int ln = o & 63, r = (o >> 6) & 3, tm = o >> 8;
+    const int mt = tm % MT, j = tm / MT;
+    const int m = 16 * mt + 4 * (ln >> 4) + r;
+    const int n = 16 * (t0 + j) + (ln & 15);
+    if (t0 + j < NT && m < M && n < N) Y[(int64_t)m * N + n] = s;
   }
 }
 
 namespace {
-template <int MT, int T>
-hipError_t go(const uint8_t *codes, const uint16_t *scales, int N, int K, const uint16_t *X,
-              int M, float *Y, hipStream_t stream) {
+
+constexpr int kCUs = 256;
+
+template <int MT, int TB>
+hipError_t go(const uint8_t *codes, const uint16_t *scales, int N, int K, const uint16_t *X, int M,
+              float *Y, hipStream_t stream) {
+  // groups in flight per wave: about 8 to 16 weight pieces, within the register file
+  constexpr int D = TB == 1 ? 8 : TB == 2 ? 6 : TB <= 4 ? 4 : 2;
   const int tiles = (N + 15) / 16;
-  const int blocks = (tiles + T - 1) / T;
-  hipLaunchKernelGGL((gemm_mfma_kernel<MT, T>), dim3(blocks), dim3(kThreads), 0, stream, codes,
+  const int blocks = (tiles + TB - 1) / TB;
+  hipLaunchKernelGGL((gemm_mfma_kernel<MT, TB, D>), dim3(blocks), dim3(kThreads), 0, stream, codes,
                      scales, X, Y, N, K, M);
   return hipGetLastError();
 }
+
+template <int MT>
+hipError_t go_tb(int TB, const uint8_t *codes, const uint16_t *scales, int N, int K,
+                 const uint16_t *X, int M, float *Y, hipStream_t s) {
+  switch (TB) {
+    case 1: return go<MT, 1>(codes, scales, N, K, X, M, Y, s);
+    case 2: return go<MT, 2>(codes, scales, N, K, X, M, Y, s);
+    case 3: return go<MT, 3>(codes, scales, N, K, X, M, Y, s);
+    case 4: return go<MT, 4>(codes, scales, N, K, X, M, Y, s);
+    case 5: return go<MT, 5>(codes, scales, N, K, X, M, Y, s);
+    case 6: return go<MT, 6>(codes, scales, N, K, X, M, Y, s);
+    case 7: return go<MT, 7>(codes, scales, N, K, X, M, Y, s);
+    default: return go<MT, 8>(codes, scales, N, K, X, M, Y, s);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_mfma(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
                             const uint16_t *X, int M, float *Y, hipStream_t stream) {
   if (M < 1 || M > 32) return hipErrorInvalidValue;
   const int n = (int)N, k = (int)K;
-  // row tiles per block: as many as keep >= 256 blocks (one per CU)
+  // column tiles per workgroup: enough for one workgroup per CU, at most 8
+  // (past that, workgroups run in rounds)
   const int tiles = (n + 15) / 16;
-  int T = 1;
-  while (T < 8 && tiles / (2 * T) >= 256) T *= 2;
-  if (M <= 16) {
-    switch (T) {
-      case 1: return go<1, 1>(codes, scales, n, k, X, M, Y, stream);
-      case 2: return go<1, 2>(codes, scales, n, k, X, M, Y, stream);
-      case 4: return go<1, 4>(codes, scales, n, k, X, M, Y, stream);
-      default: return go<1, 8>(codes, scales, n, k, X, M, Y, stream);
-    }
-  }
-  switch (T) {
-    case 1: return go<2, 1>(codes, scales, n, k, X, M, Y, stream);
-    case 2: return go<2, 2>(codes, scales, n, k, X, M, Y, stream);
-    case 4: return go<2, 4>(codes, scales, n, k, X, M, Y, stream);
-    default: return go<2, 8>(codes, scales, n, k, X, M, Y, stream);
-  }
+  const int TB = std::min((tiles + kCUs - 1) / kCUs, 8);
+  if (M <= 16) return go_tb<1>(TB, codes, scales, n, k, X, M, Y, stream);
+  return go_tb<2>(TB, codes, scales, n, k, X, M, Y, stream);
 }
 
 }  // namespace nf4

@@ -57,7 +57,7 @@ enum nf4_status {
   NF4_OK = 0,
   NF4_EINVAL = -1,  /* null pointer, N <= 0, K <= 0, K % 64 != 0 */
   NF4_EALIGN = -2,  /* codes / x / X not 16-byte aligned, scales / y not 2 / 4 */
-  NF4_ERANGE = -3,  /* M outside [1, 32], K > NF4_MAX_K, N >= 2^31, or no device */
+  NF4_ERANGE = -3,  /* M outside [1, 32], K > NF4_MAX_K, N * K / 2 >= 2^31, or no device */
   NF4_EDEVICE = -4, /* current device is not gfx950 */
   NF4_ELAUNCH = -5  /* the HIP launch itself failed */
 };

@@ -64,7 +64,8 @@ EINVAL, EALIGN, ERANGE = -1, -2, -3
 
 @pytest.mark.parametrize("N,K,expect", [(0, 64, EINVAL), (-1, 64, EINVAL), (4, 0, EINVAL),
                                         (4, 100, EINVAL), (4, 65, EINVAL), (4, 32768 + 64, ERANGE),
-                                        (2 ** 31, 64, ERANGE)])
+                                        (2 ** 31, 64, ERANGE), (2 ** 17, 32768, ERANGE),
+                                        (2 ** 26, 64, ERANGE)])
 def test_shape_validation(lib, N, K, expect):
     assert lib.nf4_gemv(P, P, N, K, P, P, NULL) == expect
     assert lib.nf4_gemm_smallm(P, P, N, K, P, 4, P, NULL) == expect
