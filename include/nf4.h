@@ -35,10 +35,12 @@
  * memory is touched.  Asynchronous GPU faults surface on the stream as usual.
  *
  * Numerics: nf4_pack and nf4_unpack are exact (bit-for-bit defined below).
- * nf4_gemv / nf4_gemm_smallm accumulate in fp32 with f16 products; per output
- * element |Y - Y_exact| <= 2e-3 * sum_k |w~(n,k) X[m][k]| + 1e-5 for finite
- * inputs whose products stay in range.  Results are deterministic: the same
- * call on the same device gives the same bits.
+ * nf4_gemv / nf4_gemm_smallm accumulate in fp32.  Below M = 8 the levels are
+ * f16 and each activation block is scaled by a power of two into f16; from
+ * M = 8 the levels are split into bf16 hi + lo and the bf16 activations are used
+ * as they are.  Per output element |Y - Y_exact| <= 2e-3 * sum_k |w~(n,k) X[m][k]|
+ * + 1e-5 for finite inputs whose products stay in range.  Results are
+ * deterministic: the same call on the same device gives the same bits.
  */
 #ifndef NF4_H
 #define NF4_H
