@@ -2,10 +2,12 @@
 """NF4 fused dequant-GEMV benchmark on one MI355X.
 
 A step is one decode pass over the linear layers of a model-shaped layer set:
-for every layer, every projection's packed NF4 weights are multiplied with its
-own activations (q, k, v, o, gate, up, down in order, one stream).  Weights are
-packed once before timing (the quantizer is offline work); the step moves the
-packed codes and scales, the bf16 activations and the fp32 outputs.
+for every layer, every projection's packed NF4 weights are multiplied with the
+layer's activations, in order, on one stream.  Projections that read the same
+activations (q|k|v, gate|up) run as one product over their rows concatenated
+along N (free in the row-major layout); --unfused launches them one by one.
+Weights are packed once before timing (the quantizer is offline work); the step
+moves the packed codes and scales, the bf16 activations and the fp32 outputs.
 
 Default workload: Llama-2-7B shapes, 32 layers of distinct seeded weights
 (3.44 GB packed, well beyond the 256 MB last-level cache), M = 1.
@@ -44,6 +46,8 @@ def parse():
     ap.add_argument("--m", type=int, default=1, help="activation rows per product")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = set's)")
     ap.add_argument("--eager", action="store_true", help="time plain launches, no HIP graph")
+    ap.add_argument("--unfused", action="store_true",
+                    help="launch q, k, v and gate, up separately instead of per same-x group")
     ap.add_argument("--event-launches", type=int, default=64,
                     help="launches per projection for the per-kernel event timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -149,17 +153,23 @@ def main():
     t0 = time.perf_counter()
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     st_any = torch.zeros(1, dtype=torch.int32, device=dev)
+    groups_ = wl.launch_groups(set_, fused=not args.unfused)
     items = []
     for layer in range(L):
-        for proj, N, K in set_.projections:
-            W = wl.weights(N, K, set_.sigma, wl.seed_for(set_.name, layer, proj, "W"), dev)
+        for name, projs in groups_:
+            K = projs[0][2]
+            N = sum(n for _, n, _ in projs)
             codes, scales = nf4.empty_packed(N, K, dev)
-            nf4.nf4_pack(W, codes, scales, status)
-            st_any.bitwise_or_(status)
-            del W
-            X = wl.activations(M, K, wl.seed_for(set_.name, layer, proj, "x"), dev)
+            r0 = 0
+            for proj, n, _ in projs:
+                W = wl.weights(n, K, set_.sigma, wl.seed_for(set_.name, layer, proj, "W"), dev)
+                nf4.nf4_pack(W, codes[r0:r0 + n], scales[r0:r0 + n], status)
+                st_any.bitwise_or_(status)
+                del W
+                r0 += n
+            X = wl.activations(M, K, wl.seed_for(set_.name, layer, name, "x"), dev)
             Y = torch.empty((M, N), dtype=torch.float32, device=dev)
-            items.append((proj, N, K, codes, scales, X, Y))
+            items.append((name, N, K, codes, scales, X, Y))
     torch.cuda.synchronize()
     if int(st_any.item()) != 0:
         raise SystemExit(f"nf4_pack flagged groups: {int(st_any.item()):#x}")
@@ -223,7 +233,7 @@ def main():
     # (rotating through the layers) replayed between two HIP events on the stream
     # the kernels run on; duration = elapsed / R (graph nodes run back to back)
     per_proj = {}
-    order = [p for p, _, _ in set_.projections]
+    order = [name for name, _ in groups_]
     for proj in order:
         its = [it for it in items if it[0] == proj]
         nl = max(1, min(args.event_launches, 4 * len(its)))
@@ -293,6 +303,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{set_.name} layer set, M={M}", "layers": L,
                    "projections": [[p, N, K] for p, N, K in set_.projections],
+                   "launches": [[name, sum(n for _, n, _ in pr), pr[0][2]] for name, pr in groups_],
+                   "schedule": ("one launch per projection" if args.unfused else
+                                "same-x projections fused along N (q|k|v, gate|up)"),
                    "m": M, "packed_gb": round(packed_bytes / 1e9, 3),
                    "step_algorithmic_mb": round(step_bytes / 1e6, 3),
                    "timing": "hip-graph replay" if graph is not None else "eager launches"},
@@ -302,8 +315,7 @@ def main():
         "per_projection": per_proj,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": (recorded_traffic("gemv_valu_kernel M=1 llama2-7b q,k,v,o,gate,up")
-                                 if (M == 1 and set_.name == "llama2-7b") else None),
+                     "traffic": recorded_traffic(f"M={M} {set_.name} " + ",".join(dom["projs"])),
                      "kernel": f"gemv_valu_kernel (M={M}, K={dom_k})" if M < 8 else
                                f"gemm_mfma_kernel (M={M}, K={dom_k})",
                      "projections": dom["projs"],

@@ -236,21 +236,48 @@ def _full_size_case(nf4, set_, proj, N, K, M):
     del W
 
 
+def _launch_shapes(set_):
+    """(name, N, K) of every distinct product shape of a layer, one launch per
+    projection and with same-x projections fused along N."""
+    seen, out = set(), []
+    for fused in (False, True):
+        for name, projs in wl.launch_groups(set_, fused):
+            N, K = sum(n for _, n, _ in projs), projs[0][2]
+            if (N, K) not in seen:
+                seen.add((N, K))
+                out.append((name, N, K))
+    return out
+
+
 @pytest.mark.parametrize("set_", [wl.SET_7B, wl.SET_13B, wl.SET_70B], ids=lambda s: s.name)
 def test_full_size_layer_shapes_m1(nf4, set_):
-    seen = set()
-    for proj, N, K in set_.projections:
-        if (N, K) in seen:
-            continue
-        seen.add((N, K))
-        _full_size_case(nf4, set_, proj, N, K, 1)
+    for name, N, K in _launch_shapes(set_):
+        _full_size_case(nf4, set_, name, N, K, 1)
 
 
 @pytest.mark.parametrize("M", [4, 8, 32])
 def test_full_size_smallm_8b(nf4, M):
-    seen = set()
-    for proj, N, K in wl.SET_8B_SMALLM.projections:
-        if (N, K) in seen:
-            continue
-        seen.add((N, K))
-        _full_size_case(nf4, wl.SET_8B_SMALLM, proj, N, K, M)
+    for name, N, K in _launch_shapes(wl.SET_8B_SMALLM):
+        _full_size_case(nf4, wl.SET_8B_SMALLM, name, N, K, M)
+
+
+def test_pack_into_row_slices_of_a_fused_matrix(nf4):
+    """q, k, v packed one by one into row ranges of one buffer equal the oracle's
+    packing of the concatenated matrix, and the fused product matches the oracle."""
+    K, parts = 512, (96, 32, 32)
+    Ws = [wl.weights(n, K, 0.02, seed=40 + i, device=DEV) for i, n in enumerate(parts)]
+    codes, scales = nf4.empty_packed(sum(parts), K, DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    r0 = 0
+    for W in Ws:
+        nf4.nf4_pack(W, codes[r0:r0 + W.shape[0]], scales[r0:r0 + W.shape[0]], st)
+        r0 += W.shape[0]
+    torch.cuda.synchronize()
+    ref_p, ref_s, _ = _host_pack(torch.cat(Ws))
+    assert np.array_equal(codes.cpu().numpy(), ref_p)
+    assert np.array_equal(_u16(scales), ref_s)
+    x = wl.activations(1, K, seed=44, device=DEV)
+    y = nf4.gemv(codes, scales, x[0])
+    torch.cuda.synchronize()
+    yr, A = oracle.gemm(ref_p, ref_s, wl.bf16_bits(x))
+    _check_product(y.reshape(1, -1), yr, A, "fused q|k|v")

@@ -45,6 +45,34 @@ SET_8B_SMALLM = LayerSet("llama3.1-8b-smallm", tuple(LLAMA31_8B), 32, 0.02, (4, 
 ALL_SETS = {s.name: s for s in (SINGLE_4096, SET_7B, SET_13B, SET_70B, SET_8B_SMALLM)}
 
 
+# Projections of one decoder layer that read the same activation vector: q, k and v
+# all take the attention input, gate and up both take the MLP input.  In the
+# row-major packed layout such a group is one matrix concatenated along N.
+SAME_X_GROUPS = (("q", "k", "v"), ("gate", "up"))
+
+
+def launch_groups(set_: "LayerSet", fused: bool):
+    """One layer's products in order, as (name, ((proj, N, K), ...)): with
+    `fused`, the same-x projections form one product over their concatenated rows."""
+    projs = list(set_.projections)
+    if not fused:
+        return [(p, ((p, N, K),)) for p, N, K in projs]
+    out = []
+    i = 0
+    while i < len(projs):
+        for grp in SAME_X_GROUPS:
+            names = tuple(p for p, _, _ in projs[i:i + len(grp)])
+            if names == grp and len({K for _, _, K in projs[i:i + len(grp)]}) == 1:
+                out.append(("|".join(grp), tuple(projs[i:i + len(grp)])))
+                i += len(grp)
+                break
+        else:
+            p, N, K = projs[i]
+            out.append((p, ((p, N, K),)))
+            i += 1
+    return out
+
+
 def _mix(*parts) -> int:
     """SplitMix64-style mixing of integers into a 63-bit seed."""
     h = BASE_SEED
