@@ -12,29 +12,34 @@
 // registers as f16 pairs for the whole kernel.  Rows are dealt round-robin over
 // the grid, so at any moment all CUs stream one contiguous band of rows.  Per row
 // a lane issues UPL 128-bit code loads (consecutive lanes on consecutive 16-byte
-// chunks) and one or two 2-byte scale loads that cover the wave's groups; each
-// unit's scale is then fetched from the loading lane with ds_bpermute.  A ring of
-// kDepth rows per wave keeps the loads in flight; loads carry no branches (a
-// branch around a load makes the compiler wait for every load in flight before
-// the register can be reused).
+// chunks) and one 32-bit scale load (two scales) that covers the wave's groups;
+// each unit's scale is then fetched from the loading lane with ds_bpermute.
+// Loads are buffer loads: the row offset is a scalar and the per-lane offsets are
+// fixed registers, so the address unit gets no per-row vector arithmetic.  A
+// short ring of rows per wave keeps the next loads in flight; no load sits behind
+// a branch and no register a load in flight reads is rewritten early, so the
+// compiler's waits cover exactly the row being consumed.
 //
 // Decode: one v_perm_b32 turns a code byte into the LDS address of its entry in
 // the bank-replicated byte table (nf4_device.h); the entry is the f16 pair
 // (L[lo], L[hi]) and feeds one v_dot2_f32_f16 against (x[2j], x[2j+1]).  Two
-// weights cost one perm, one LDS read and one dot per activation row; the group
-// scale is applied once per unit in fp32.
+// weights cost one perm, one LDS read and one dot per activation row; the table
+// reads run two code words ahead of the dots; the group scale is applied once per
+// unit in fp32.
 //
-// Activations are converted once per workgroup: thread t turns unit t of each
-// activation row into f16 after scaling it by a power of two that puts its
-// largest |x| just under 2^15 (exact from bf16 down to 2^-29 of that maximum),
-// and stages it in LDS with the shift; lanes then copy their units into
+// Activations are converted once per workgroup: X is read in coalesced 16-byte
+// chunks, each 32-value unit is scaled by a power of two that puts its largest
+// |x| just under 2^15 (exact from bf16 down to 2^-29 of that maximum), converted
+// to f16 and staged in LDS with the shift; lanes then copy their units into
 // registers.  The shift is undone on the unit's fp32 partial.  Activation loads
 // are issued before the first code loads so that the set-up does not wait
 // behind them (loads return in order).
 //
 // Reduction: per row, lanes are summed with DPP row operations in a fixed order;
-// the S slices of a row are added in LDS in slice order.  No atomics: results
-// are bitwise reproducible.
+// row results wait in LDS and the S slices of a row are added in slice order
+// when every row is done.  No atomics: results are bitwise reproducible.
+#include <type_traits>
+
 #include "nf4_device.h"
 #include "nf4_launch.h"
 
@@ -53,13 +58,18 @@ constexpr int kRedFloats = 4096;                        // cross-slice partials 
 constexpr int kStageBytes = 163840 - 4 * kLutWords - 4 * kRedFloats;  // 80 KiB for activations
 constexpr int kUnitStageBytes = 64 + 4;                 // 32 f16 + a shift, per (row, unit)
 constexpr int kMaxUnits = 1024;                         // K <= 32768
+// activation chunks (16 bytes) per thread: all of M * K fits the stage in one go
+constexpr int kXChunks = (kStageBytes / kUnitStageBytes * 4 + kThreads - 1) / kThreads;
 
-template <int M, int UPL>
+template <int M, int UPL, bool WS>
 __global__ void __launch_bounds__(kThreads)
     gemv_valu_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
                      const uint16_t *__restrict__ X, float *__restrict__ Y, int N, int K, int S,
                      int G, int Us, int iters) {
-  constexpr int kDepth = 4;  // rows of codes in flight per wave (registers)
+  // rows of codes in flight per wave (registers).  Two for M = 1: measured
+  // deeper rings run slower, since a wave whose next load waits for room at the
+  // address unit cannot go on to compute rows whose data has arrived.
+  constexpr int kDepth = M > 1 ? 4 : 2;
   // one LDS block carved by hand so that the decode table starts at offset 0: its
   // byte addresses (< 64 KiB) then need no base added before each read
   __shared__ __attribute__((aligned(16))) uint32_t lds[kLutWords + kRedFloats + kStageBytes / 4];
@@ -73,6 +83,7 @@ __global__ void __launch_bounds__(kThreads)
   const int slice = wave % S;
   const int grp = wave / S;  // S * G == 8: every wave streams rows
   const int U = K >> 5;
+  __builtin_assume(U > 0 && U <= kMaxUnits);  // lets index math use 24-bit multiplies
   const int ub = slice * Us;
   const int ue = min(U, ub + Us);
   const int rows_per_block = G * iters;
@@ -92,169 +103,237 @@ __global__ void __launch_bounds__(kThreads)
     valid[i] = unit[i] < ue;
     uload[i] = valid[i] ? unit[i] : 0;
   }
-  // scales: lane l loads the scales of groups ub/2 + l (+ 64); Us is a multiple
-  // of 4, so a slice owns whole groups, at most 128 of them.  Unit ub + l + 64 i
-  // reads its scale from lane (l/2 + 32 i) mod 64 of load i / 2.
-  constexpr int kScaleLoads = (UPL + 1) / 2;
+  // scales.  Us is a multiple of 4, so a slice owns whole groups, at most 128 of
+  // them, starting at an even group gb.  Unit ub + l + 64 i needs group
+  // gb + l/2 + 32 i.
+  //  WS (even group count, 4-byte aligned scales): lane l loads the 32-bit word
+  //    holding groups gb + 2l and gb + 2l + 1, one load per row for the whole
+  //    slice; unit i reads word l/4 + 16 i from its lane and takes half (l/2) & 1.
+  //  otherwise: lane l loads the 2-byte scale of group gb + l (+ 64); unit i
+  //    reads it from lane (l/2 + 32 i) mod 64 of load i / 2.
+  // (32-bit words matter: a 16-bit value kept in a register ring across loop
+  // iterations gets repacked at the back edge, which waits for the load.)
+  constexpr int kScaleLoads = WS ? 1 : (UPL + 1) / 2;
+  using ScaleT = typename std::conditional<WS, uint32_t, uint16_t>::type;
   const int gb = ub >> 1;
   int gload[kScaleLoads];
 #pragma unroll
-  for (int j = 0; j < kScaleLoads; ++j) gload[j] = min(gb + lane + 64 * j, (int)row_groups - 1);
+  for (int j = 0; j < kScaleLoads; ++j)
+    gload[j] = WS ? min((gb >> 1) + lane, (int)(row_groups >> 1) - 1)
+                  : min(gb + lane + 64 * j, (int)row_groups - 1);
   int sperm[UPL];
 #pragma unroll
-  for (int i = 0; i < UPL; ++i) sperm[i] = ((lane >> 1) + 32 * (i & 1)) * 4;
+  for (int i = 0; i < UPL; ++i)
+    sperm[i] = WS ? ((lane >> 2) + 16 * i) * 4 : ((lane >> 1) + 32 * (i & 1)) * 4;
 
-  // ---- activations, pass 0: loads first (they must not queue behind codes)
-  const int per_pass = kStageBytes / (M * kUnitStageBytes);
-  const int npass = (U + per_pass - 1) / per_pass;
-  // (row, unit) items per thread and pass: a pass holds at most kStageBytes
-  constexpr int kPassItems = kStageBytes / kUnitStageBytes;
-  constexpr int kItems = ((M * kMaxUnits < kPassItems ? M * kMaxUnits : kPassItems) + kThreads - 1) /
-                         kThreads;
-  uint4 xraw[kItems][4];
-  auto load_x = [&](int u0, int nu) {
+  // ---- activations, loads first (they must not queue behind codes).  X [M][K]
+  // is read as 16-byte chunks of 8 values, consecutive threads on consecutive
+  // chunks; chunk c is quarter c % 4 of unit (c / 4) % U of row c / (4 U).
+  // Threads past the end load the last chunk again (no branch around loads).
+  const int nchunks = M * U * 4;
+  // The decode table goes first: it needs no memory, and built later it would
+  // queue behind the loads for the address unit.
+  build_byte_lut(lut, tid, kThreads);
+
+  // A wave issues only the chunk loads it needs (the branch is uniform per wave).
+  uint4 xr[kXChunks];
+  const int wave_chunk0 = tid & ~63;
 #pragma unroll
-    for (int j = 0; j < kItems; ++j) {
-      // no branch around the loads (see above): threads past the end load the
-      // pass's last item again
-      const int it = min(tid + j * kThreads, M * nu - 1);
-      const int m = it / nu;
-      const int uu = it - m * nu;
-      const uint4 *src = reinterpret_cast<const uint4 *>(X + (int64_t)m * K + (u0 + uu) * 32);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) xraw[j][q] = src[q];
+  for (int j = 0; j < kXChunks; ++j) {
+    if (wave_chunk0 + j * kThreads < nchunks) {
+      const int c = min(tid + j * kThreads, nchunks - 1);
+      xr[j] = *reinterpret_cast<const uint4 *>(X + (int64_t)c * 8);
     }
-  };
-  load_x(0, min(per_pass, U));
+  }
 
   // ---- rows: the first kDepth rows of codes go out before any set-up work
   const int row_first = min(row0 + grp, N - 1);
-  // the row is the same for the whole wave: its base address lives in scalar
-  // registers and each load takes a 32-bit per-lane offset (no vector address math)
-  auto load_row = [&](int r, uint4 *c, uint32_t *s) {
-    const int rr = __builtin_amdgcn_readfirstlane(r < N ? r : row_first);  // past the end:
-    const uint8_t *crow = codes + (int64_t)rr * row_bytes;     // the wave's own first row
-    const uint16_t *srow = scales + (int64_t)rr * row_groups;
+  // Buffer loads: the row offset is a scalar, the per-lane offsets are fixed
+  // registers, so no vector address arithmetic runs per row and no register a
+  // load in flight still reads is ever rewritten.  Matrices are below 2 GiB.
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(codes), 0, (int)((int64_t)N * row_bytes), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(scales), 0, (int)((int64_t)N * row_groups * 2), kBufferWord3);
+  int cvo[UPL], svo[kScaleLoads];
 #pragma unroll
-    for (int i = 0; i < UPL; ++i)
-      c[i] = *reinterpret_cast<const uint4 *>(crow + (uint32_t)(uload[i] * 16));
+  for (int i = 0; i < UPL; ++i) cvo[i] = uload[i] * 16;
 #pragma unroll
-    for (int j = 0; j < kScaleLoads; ++j) s[j] = srow[(uint32_t)gload[j]];
+  for (int j = 0; j < kScaleLoads; ++j) svo[j] = gload[j] * (WS ? 4 : 2);
+  // Step t of the wave is row r; a step past the wave's last (or a row past N)
+  // loads row `fallback` instead, one the wave has just read, so the spare load
+  // hits in cache.
+  auto load_row = [&](int t, int r, int fallback, uint4 *c, ScaleT *s) {
+    const int rr = __builtin_amdgcn_readfirstlane((t < iters && r < N) ? r : fallback);
+    const int coff = rr * (int)row_bytes;
+    const int soff = rr * (int)row_groups * 2;
+#pragma unroll
+    for (int i = 0; i < UPL; ++i) {
+      const u32x4_nt_t v = __builtin_amdgcn_raw_buffer_load_b128(crs, cvo[i], coff, kLoadStream);
+      c[i] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+#pragma unroll
+    for (int j = 0; j < kScaleLoads; ++j) {
+      if constexpr (WS)
+        s[j] = __builtin_amdgcn_raw_buffer_load_b32(srs, svo[j], soff, 0);
+      else
+        s[j] = __builtin_amdgcn_raw_buffer_load_b16(srs, svo[j], soff, 0);
+    }
   };
   uint4 cb[kDepth][UPL];
-  uint32_t sb[kDepth][kScaleLoads];
+  ScaleT sb[kDepth][kScaleLoads];
+  // (rows issued in the same order as in the loop, so that the load counts the
+  // compiler waits on agree on both paths into the loop)
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d) load_row(row0 + grp + d * rstride, cb[d], sb[d]);
+  for (int d = 0; d < kDepth; ++d) {
+    load_row(d, row0 + grp + d * rstride, row_first, cb[d], sb[d]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
-  build_byte_lut(lut, tid, kThreads);
-
-  // ---- activations: convert, stage, copy into registers (pass by pass)
+  // ---- activations: convert, stage, copy into registers.  Each unit is scaled
+  // by its own power of two (the largest |x| of its 32 values, a max over the 4
+  // threads of a quad), converted to f16 and staged as stage_x[q][m][u] (uint4)
+  // with its shift in stage_sh[m][u].
   uint32_t xh[M][UPL][16];
   float xf[M][UPL];  // 2^-shift of each unit
-  uint4 *stage_x = reinterpret_cast<uint4 *>(stage);                      // [4][M][per_pass]
-  int *stage_sh = reinterpret_cast<int *>(stage + M * per_pass * 64);     // [M][per_pass]
-  for (int pass = 0; pass < npass; ++pass) {
-    const int u0 = pass * per_pass;
-    const int nu = min(per_pass, U - u0);
-    if (pass > 0) load_x(u0, nu);
+  uint4 *stage_x = reinterpret_cast<uint4 *>(stage);                 // [4][M][U]
+  int *stage_sh = reinterpret_cast<int *>(stage + M * U * 64);       // [M][U]
 #pragma unroll
-    for (int j = 0; j < kItems; ++j) {
-      const int it = tid + j * kThreads;
-      if (it < M * nu) {
-        const int m = it / nu;
-        const int uu = it - m * nu;
-        uint32_t mx = 0;
+  for (int j = 0; j < kXChunks; ++j) {
+    const int c = tid + j * kThreads;
+    const uint4 v = xr[j];
+    uint32_t mx = max(max(bf16x2_absmax_bits(v.x), bf16x2_absmax_bits(v.y)),
+                      max(bf16x2_absmax_bits(v.z), bf16x2_absmax_bits(v.w)));
+    mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0xB1, 0xf, 0xf, false));
+    mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x4E, 0xf, 0xf, false));
+    if (c < nchunks) {  // nchunks is a multiple of 4: a quad is valid or not as a whole
+      const int sh = f16_range_shift(mx);
+      const int q = c & 3;
+      const int mu = c >> 2;  // m * U + u
+      const int m = mu / U;
+      const int u = mu - m * U;
+      stage_x[(q * M + m) * U + u] =
+          make_uint4(bf16x2_to_f16x2(v.x, sh), bf16x2_to_f16x2(v.y, sh),
+                     bf16x2_to_f16x2(v.z, sh), bf16x2_to_f16x2(v.w, sh));
+      if (q == 0) stage_sh[mu] = sh;
+    }
+  }
+  __syncthreads();
+  // (the block strides are scalars: kept out of per-lane 64-bit multiply-adds,
+  // which would read the neighbour of an offset register, here a ring register
+  // with a load in flight, and wait for it)
+  const int rows_stride = __builtin_amdgcn_readfirstlane(U);
+  const int q_stride = __builtin_amdgcn_readfirstlane(M * U);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          mx = max(mx, max(max(bf16x2_absmax_bits(xraw[j][q].x), bf16x2_absmax_bits(xraw[j][q].y)),
-                           max(bf16x2_absmax_bits(xraw[j][q].z), bf16x2_absmax_bits(xraw[j][q].w))));
-        const int sh = f16_range_shift(mx);
+  for (int m = 0; m < M; ++m)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          stage_x[(q * M + m) * per_pass + uu] = make_uint4(
-              bf16x2_to_f16x2(xraw[j][q].x, sh), bf16x2_to_f16x2(xraw[j][q].y, sh),
-              bf16x2_to_f16x2(xraw[j][q].z, sh), bf16x2_to_f16x2(xraw[j][q].w, sh));
-        stage_sh[m * per_pass + uu] = sh;
+    for (int i = 0; i < UPL; ++i) {
+      if (valid[i]) {
+        const uint4 *xs = stage_x + unit[i] + m * rows_stride;
+#pragma unroll
+        for (int q = 0; q < 4; ++q, xs += q_stride) {
+          const uint4 t = *xs;
+          xh[m][i][4 * q + 0] = t.x;
+          xh[m][i][4 * q + 1] = t.y;
+          xh[m][i][4 * q + 2] = t.z;
+          xh[m][i][4 * q + 3] = t.w;
+        }
+        xf[m][i] = ldexpf(1.0f, -stage_sh[m * rows_stride + unit[i]]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) xh[m][i][q] = 0;
+        xf[m][i] = 0.0f;
       }
     }
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-      for (int i = 0; i < UPL; ++i) {
-        const int uu = unit[i] - u0;
-        if (valid[i] && uu >= 0 && uu < nu) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint4 t = stage_x[(q * M + m) * per_pass + uu];
-            xh[m][i][4 * q + 0] = t.x;
-            xh[m][i][4 * q + 1] = t.y;
-            xh[m][i][4 * q + 2] = t.z;
-            xh[m][i][4 * q + 3] = t.w;
-          }
-          xf[m][i] = ldexpf(1.0f, -stage_sh[m * per_pass + uu]);
-        } else if (pass == 0) {
-#pragma unroll
-          for (int q = 0; q < 16; ++q) xh[m][i][q] = 0;
-          xf[m][i] = 0.0f;
-        }
-      }
-    if (pass + 1 < npass) __syncthreads();  // the next pass overwrites the stage
-  }
 
   // ---- rows
   const uint32_t laneoff = (uint32_t)lane * 4u;
-  auto compute_row = [&](int r, int step, const uint4 *c, const uint32_t *s) {
+  auto compute_row = [&](int r, int step, const uint4 *c, const ScaleT *s) {
     float acc[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+    // units outside the lane's slice: activations are 0, scale forced to 0
+    float sc[UPL];
 #pragma unroll
     for (int i = 0; i < UPL; ++i) {
-      const uint32_t q[4] = {c[i].x, c[i].y, c[i].z, c[i].w};
-      float p[M];
-#pragma unroll
-      for (int m = 0; m < M; ++m) p[m] = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t l0 = lds_load_u32(lut, lut_addr<0>(q[j], laneoff));
-        const uint32_t l1 = lds_load_u32(lut, lut_addr<1>(q[j], laneoff));
-        const uint32_t l2 = lds_load_u32(lut, lut_addr<2>(q[j], laneoff));
-        const uint32_t l3 = lds_load_u32(lut, lut_addr<3>(q[j], laneoff));
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          p[m] = dot2(l0, xh[m][i][4 * j + 0], p[m]);
-          p[m] = dot2(l1, xh[m][i][4 * j + 1], p[m]);
-          p[m] = dot2(l2, xh[m][i][4 * j + 2], p[m]);
-          p[m] = dot2(l3, xh[m][i][4 * j + 3], p[m]);
-        }
+      uint32_t sbits;
+      if constexpr (WS) {
+        const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute(sperm[i], (int)s[0]);
+        sbits = (lane & 2) ? (w >> 16) : (w & 0xffffu);
+      } else {
+        sbits = (uint32_t)__builtin_amdgcn_ds_bpermute(sperm[i], (int)(uint32_t)s[i >> 1]);
       }
-      // units outside the lane's slice: activations are 0, scale forced to 0
-      const uint32_t sbits = (uint32_t)__builtin_amdgcn_ds_bpermute(sperm[i], (int)s[i >> 1]);
-      const float sc = valid[i] ? f16_bits_to_f32(sbits) : 0.0f;
+      sc[i] = valid[i] ? f16_bits_to_f32(sbits) : 0.0f;
+    }
+    // table reads run two code words ahead of the dot products that consume them,
+    // so the LDS latency overlaps the arithmetic
+    constexpr int kWords = 4 * UPL;
+    uint32_t q[kWords];
 #pragma unroll
-      for (int m = 0; m < M; ++m) acc[m] = fmaf(p[m], sc * xf[m][i], acc[m]);
+    for (int i = 0; i < UPL; ++i) {
+      q[4 * i + 0] = c[i].x;
+      q[4 * i + 1] = c[i].y;
+      q[4 * i + 2] = c[i].z;
+      q[4 * i + 3] = c[i].w;
+    }
+    uint32_t lv[3][4];
+    auto fetch = [&](int t, uint32_t *dst) __attribute__((always_inline)) {
+      dst[0] = lds_load_u32(lut, lut_addr<0>(q[t], laneoff));
+      dst[1] = lds_load_u32(lut, lut_addr<1>(q[t], laneoff));
+      dst[2] = lds_load_u32(lut, lut_addr<2>(q[t], laneoff));
+      dst[3] = lds_load_u32(lut, lut_addr<3>(q[t], laneoff));
+    };
+    fetch(0, lv[0]);
+    if (kWords > 1) fetch(1, lv[1]);
+    float p[M];
+#pragma unroll
+    for (int t = 0; t < kWords; ++t) {
+      if (t + 2 < kWords) fetch(t + 2, lv[(t + 2) % 3]);
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the dots below
+      const int i = t >> 2, j = t & 3;
+      if (j == 0) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) p[m] = 0.0f;
+      }
+      const uint32_t *l = lv[t % 3];
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        p[m] = dot2(l[0], xh[m][i][4 * j + 0], p[m]);
+        p[m] = dot2(l[1], xh[m][i][4 * j + 1], p[m]);
+        p[m] = dot2(l[2], xh[m][i][4 * j + 2], p[m]);
+        p[m] = dot2(l[3], xh[m][i][4 * j + 3], p[m]);
+      }
+      if (j == 3) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[m] = fmaf(p[m], sc[i] * xf[m][i], acc[m]);
+      }
     }
 #pragma unroll
     for (int m = 0; m < M; ++m) {
+      // results wait in LDS until every row is done: a store inside the loop
+      // would make later register reuse wait for it, and with it for every
+      // load issued before it
       const float t = wave_sum(acc[m]);
-      if (lane == 0) {
-        if (S == 1)
-          Y[(int64_t)m * N + r] = t;
-        else
-          red[(m * rows_per_block + step * G + grp) * S + slice] = t;
-      }
+      if (lane == 0) red[(m * rows_per_block + step * G + grp) * S + slice] = t;
     }
   };
 
-  for (int it = 0; it < iters; it += kDepth) {
+  // Whole rounds of kDepth rows run without branches (rows past N compute on the
+  // wave's first row and are never stored), so the load waits stay exact across
+  // the loop's back edge; the last partial round follows.
+  int it = 0;
+  for (; it + kDepth <= iters; it += kDepth) {
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
       const int r = row0 + grp + (it + d) * rstride;
-      if (it + d < iters && r < N) compute_row(r, it + d, cb[d], sb[d]);
-      load_row(r + kDepth * rstride, cb[d], sb[d]);
+      compute_row(r, it + d, cb[d], sb[d]);
+      load_row(it + d + kDepth, r + kDepth * rstride, min(r, N - 1), cb[d], sb[d]);
     }
   }
-  if (S > 1) {
+#pragma unroll
+  for (int d = 0; d < kDepth - 1; ++d)
+    if (it + d < iters) compute_row(row0 + grp + (it + d) * rstride, it + d, cb[d], sb[d]);
+  {
     __syncthreads();
     for (int t = tid; t < M * rows_per_block; t += kThreads) {
       const int m = t / rows_per_block;
@@ -285,7 +364,7 @@ int upl_cap(int M) { return M == 1 ? 4 : (M == 2 ? 3 : (M <= 4 ? 2 : 1)); }
 // Choose slices / row groups / rows per workgroup for an (N, K, M) product.
 bool plan_valu(int64_t N, int64_t K, int M, Plan &p) {
   const int U = (int)(K / 32);
-  if (U > kMaxUnits) return false;
+  if (U > kMaxUnits || M * U * kUnitStageBytes > kStageBytes) return false;
   int S = 1;  // a power of two, so that S * G covers the 8 waves exactly
   while (S < cdiv(U, 64 * upl_cap(M))) S *= 2;
   if (S > kWaves) return false;
@@ -296,8 +375,8 @@ bool plan_valu(int64_t N, int64_t K, int M, Plan &p) {
   const int upl = cdiv(Us, 64);
   // rows per workgroup: G * iters, about N / (number of CUs)
   int iters = std::max(1, cdiv(N, (int64_t)G * kCUs));
-  while (iters > 1 && S > 1 && M * G * iters * S > kRedFloats) --iters;
-  if (S > 1 && M * G * iters * S > kRedFloats) return false;
+  while (iters > 1 && M * G * iters * S > kRedFloats) --iters;
+  if (M * G * iters * S > kRedFloats) return false;
   p.S = S;
   p.G = G;
   p.Us = Us;
@@ -310,8 +389,14 @@ bool plan_valu(int64_t N, int64_t K, int M, Plan &p) {
 template <int M, int UPL>
 hipError_t go(const Plan &p, const uint8_t *codes, const uint16_t *scales, int N, int K,
               const uint16_t *X, float *Y, hipStream_t stream) {
-  hipLaunchKernelGGL((gemv_valu_kernel<M, UPL>), dim3(p.blocks), dim3(kThreads), 0, stream, codes,
-                     scales, X, Y, N, K, p.S, p.G, p.Us, p.iters);
+  // 32-bit scale words need an even group count and a 4-byte aligned array
+  const bool ws = ((K >> 6) % 2 == 0) && ((reinterpret_cast<uintptr_t>(scales) & 3) == 0);
+  if (ws)
+    hipLaunchKernelGGL((gemv_valu_kernel<M, UPL, true>), dim3(p.blocks), dim3(kThreads), 0, stream,
+                       codes, scales, X, Y, N, K, p.S, p.G, p.Us, p.iters);
+  else
+    hipLaunchKernelGGL((gemv_valu_kernel<M, UPL, false>), dim3(p.blocks), dim3(kThreads), 0, stream,
+                       codes, scales, X, Y, N, K, p.S, p.G, p.Us, p.iters);
   return hipGetLastError();
 }
 

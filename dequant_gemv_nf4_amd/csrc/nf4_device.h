@@ -86,6 +86,18 @@ __device__ __forceinline__ uint32_t lut_addr(uint32_t codeword, uint32_t laneoff
   return __builtin_amdgcn_perm(codeword, laneoff, sel);
 }
 
+// Buffer resource word 3 for raw (untyped) buffer access on gfx9-family parts,
+// and the cache-policy operand of a streamed (read-once) load: non-temporal.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kLoadStream = 2;
+
+// 16-byte load of streamed data (read once): non-temporal hint
+typedef uint32_t u32x4_nt_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream16(const void *p) {
+  const u32x4_nt_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt_t *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ uint32_t lds_load_u32(const uint32_t *base, uint32_t byte_addr) {
   return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(base) + byte_addr);
 }
