@@ -65,6 +65,10 @@ def lib():
         L.orc_gemm_rows.restype = None
         L.orc_gemm_rows.argtypes = [_u8p, _u16p, _i64, _i64, _u16p, _i64, _i64p,
                                     _i64, _f64p, _f64p]
+        L.orc_f64_to_bf16_bits.restype = ctypes.c_uint16
+        L.orc_f64_to_bf16_bits.argtypes = [ctypes.c_double]
+        L.orc_embed.restype = ctypes.c_int32
+        L.orc_embed.argtypes = [_u8p, _u16p, _i64, _i64, _i64p, _i64, _u16p]
         _lib = L
     return _lib
 
@@ -192,3 +196,24 @@ def within_tolerance(y, y_ref, absum):
     """Boolean mask of elements meeting the per-element tolerance (fp64 bound)."""
     y = np.asarray(y, np.float64)
     return np.abs(y - y_ref) <= REL_TOL * absum + ABS_TOL
+
+
+def f64_to_bf16_bits(v: float) -> int:
+    """Nearest bfloat16 to v (ties to even), as bits; NaN -> 0x7FC0."""
+    return int(lib().orc_f64_to_bf16_bits(float(v)))
+
+
+EMBED_BAD_ID = 1
+
+
+def embed(packed, scales, ids):
+    """Rows ids of the dequantised matrix rounded once to bf16 -> (uint16 bits
+    [T][K], status).  Out-of-range ids give zero rows and status EMBED_BAD_ID."""
+    packed = _c(packed, np.uint8)
+    scales = _c(scales, np.uint16)
+    ids = _c(ids, np.int64).reshape(-1)
+    N, K = packed.shape[0], packed.shape[1] * 2
+    out = np.empty((ids.size, K), np.uint16)
+    st = lib().orc_embed(_p(packed, _u8p), _p(scales, _u16p), N, K, _p(ids, _i64p),
+                         ids.size, _p(out, _u16p))
+    return out, int(st)

@@ -281,3 +281,60 @@ extern "C" void orc_gemm_rows(const uint8_t *packed, const uint16_t *scales, int
     }
   (void)N;
 }
+
+// ---------------------------------------------------------------------------
+// Rounding to bfloat16 (8 significant bits, the binary32 exponent range): the
+// nearest bf16 value to v, ties to the even significand.  Written out on the
+// exact value: the significand scaled to an integer range, rounded by hand.
+extern "C" uint16_t orc_f64_to_bf16_bits(double v) {
+  if (std::isnan(v)) return 0x7FC0;
+  const uint16_t sign = std::signbit(v) ? 0x8000 : 0;
+  const double a = std::fabs(v);
+  if (std::isinf(a)) return sign | 0x7F80;
+  if (a == 0.0) return sign;
+  // a = q * 2^e2 with q an integer multiple of the bf16 spacing at a's binade:
+  // normal range (a >= 2^-126): 8 significant bits; below, spacing 2^-133.
+  int e = 0;
+  (void)std::frexp(a, &e);                 // a in [2^(e-1), 2^e)
+  int e2 = (e - 1 >= -126) ? (e - 8) : -133;  // spacing of bf16 values near a
+  const double q = std::ldexp(a, -e2);     // exact: a power-of-two scaling
+  double fl = std::floor(q);
+  const double rem = q - fl;               // exact
+  if (rem > 0.5 || (rem == 0.5 && std::fmod(fl, 2.0) != 0.0)) fl += 1.0;
+  const double r = std::ldexp(fl, e2);     // the rounded value, exactly a bf16
+  if (r >= std::ldexp(1.0, 128)) return sign | 0x7F80;  // rounds past the largest
+  const float f = (float)r;                // exact: every bf16 value is a binary32
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return sign | (uint16_t)((u >> 16) & 0x7FFF);
+}
+
+// ---------------------------------------------------------------------------
+// Packed embedding rows: decode only the requested rows (deep-fold README,
+// Method: embeddings decode the requested rows), w~ = L[c] * s exact in fp64,
+// then one rounding to bf16.  An id outside [0, N) yields a zero row and the
+// status bit.
+extern "C" int32_t orc_embed(const uint8_t *packed, const uint16_t *scales, int64_t N,
+                             int64_t K, const int64_t *ids, int64_t T, uint16_t *out) {
+  double lv64[16];
+  float lv32[16];
+  orc_codebook(lv64, lv32);
+  int32_t status = 0;
+  const int64_t G = K / 64;
+  for (int64_t t = 0; t < T; ++t) {
+    const int64_t n = ids[t];
+    uint16_t *o = out + t * K;
+    if (n < 0 || n >= N) {
+      status |= ORC_EMBED_BAD_ID;
+      for (int64_t k = 0; k < K; ++k) o[k] = 0;
+      continue;
+    }
+    for (int64_t k = 0; k < K; ++k) {
+      const uint8_t byte = packed[n * (K / 2) + k / 2];
+      const int c = (k % 2 == 0) ? (byte & 15) : (byte >> 4);
+      const double s = orc_f16_bits_to_f64(scales[n * G + k / 64]);
+      o[k] = orc_f64_to_bf16_bits((double)lv32[c] * s);
+    }
+  }
+  return status;
+}

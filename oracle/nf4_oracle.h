@@ -76,6 +76,21 @@ void orc_gemm_rows(const uint8_t *packed, const uint16_t *scales, int64_t N,
                    int64_t K, const uint16_t *X, int64_t M, const int64_t *rows,
                    int64_t nrows, double *Y, double *A);
 
+/* exact value -> bfloat16 bits, one rounding to nearest, ties to even (8
+ * significant bits, binary32 exponent range, subnormals kept); any NaN gives
+ * the quiet NaN 0x7FC0. */
+uint16_t orc_f64_to_bf16_bits(double v);
+
+/* status bit written by orc_embed */
+#define ORC_EMBED_BAD_ID 1 /* an id outside [0, N): that output row is zero */
+
+/* Packed embedding rows (deep-fold README: embeddings decode only the requested
+ * rows): out[t][k] = bf16(w~[ids[t]][k]) for t < T, w~ = L[c] * s exact, one
+ * rounding.  out is bf16 bits [T][K].  Returns ORC_EMBED_BAD_ID if any id is
+ * out of range (those rows are all +0), else 0. */
+int32_t orc_embed(const uint8_t *packed, const uint16_t *scales, int64_t N, int64_t K,
+                  const int64_t *ids, int64_t T, uint16_t *out);
+
 #ifdef __cplusplus
 }
 #endif
