@@ -14,14 +14,17 @@ from ._lib import (  # noqa: F401
     GROUP,
     MAX_K,
     MAX_M,
+    EMBED_BAD_ID,
     NF4Error,
     PACK_NONFINITE,
     PACK_SCALE_OVERFLOW,
+    embed,
     empty_packed,
     gemm,
     gemv,
     lib_path,
     nf4_codebook,
+    nf4_embed,
     nf4_gemm_smallm,
     nf4_gemv,
     nf4_pack,

@@ -14,6 +14,7 @@ MAX_M = 32
 MAX_K = 32768
 PACK_NONFINITE = 1
 PACK_SCALE_OVERFLOW = 2
+EMBED_BAD_ID = 1
 
 _STATUS = {0: "NF4_OK", -1: "NF4_EINVAL", -2: "NF4_EALIGN", -3: "NF4_ERANGE",
            -4: "NF4_EDEVICE", -5: "NF4_ELAUNCH"}
@@ -44,7 +45,8 @@ def _load():
     L.nf4_unpack.argtypes = [vp, vp, i64, i64, vp, vp]
     L.nf4_gemv.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     L.nf4_gemm_smallm.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp]
-    for f in (L.nf4_pack, L.nf4_unpack, L.nf4_gemv, L.nf4_gemm_smallm):
+    L.nf4_embed.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, vp]
+    for f in (L.nf4_pack, L.nf4_unpack, L.nf4_gemv, L.nf4_gemm_smallm, L.nf4_embed):
         f.restype = ctypes.c_int
     L.nf4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
     L.nf4_codebook.restype = None
@@ -150,6 +152,24 @@ def nf4_gemm_smallm(codes, scales, X, Y, stream=None):
                                                           _stream(X.device, stream)))
 
 
+def nf4_embed(codes, scales, K, ids, out, dev_status=None, stream=None):
+    """out bf16 [T][K] = rows ids (int64 [T]) of dequant(codes, scales), rounded once."""
+    _need(codes, "codes", (torch.uint8,), (2,))
+    _need(scales, "scales", _U16 + (torch.float16,))
+    _need(ids, "ids", (torch.int64,), (1,))
+    _need(out, "out", _BF16, (2,))
+    N = _nk(codes, scales, K)
+    T = ids.numel()
+    if tuple(out.shape) != (T, K):
+        raise ValueError(f"out must be [T={T}][K={K}]")
+    if dev_status is not None:
+        _need(dev_status, "dev_status", (torch.int32,))
+    with torch.cuda.device(codes.device):
+        _check("nf4_embed", _load().nf4_embed(_ptr(codes), _ptr(scales), N, K, _ptr(ids), T,
+                                              _ptr(out), _ptr(dev_status),
+                                              _stream(codes.device, stream)))
+
+
 def nf4_codebook():
     """The library's 16 fp32 NF4 levels (host call, no GPU needed)."""
     out = (ctypes.c_float * 16)()
@@ -187,6 +207,12 @@ def gemv(codes, scales, x, stream=None):
     y = torch.empty(codes.shape[0], dtype=torch.float32, device=x.device)
     nf4_gemv(codes, scales, x, y, stream)
     return y
+
+
+def embed(codes, scales, K, ids, stream=None):
+    out = torch.empty((ids.numel(), K), dtype=torch.bfloat16, device=codes.device)
+    nf4_embed(codes, scales, K, ids, out, None, stream)
+    return out
 
 
 def gemm(codes, scales, X, stream=None):

@@ -88,6 +88,19 @@ int nf4_gemv(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
   return nf4_gemm_smallm(codes, scales, N, K, x, 1, y, stream);
 }
 
+int nf4_embed(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+              const int64_t *ids, int64_t T, uint16_t *out, int32_t *dev_status, void *stream) {
+  if (!codes || !scales || T < 0 || (T > 0 && (!ids || !out))) return NF4_EINVAL;
+  if (int r = check_shape(N, K)) return r;
+  if (T > nf4::embed_max_rows(K)) return NF4_ERANGE;
+  if (!aligned(codes, 4) || !aligned(scales, 2) || (T > 0 && (!aligned(ids, 8) ||
+      !aligned(out, 16))) || (dev_status && !aligned(dev_status, 4)))
+    return NF4_EALIGN;
+  if (int r = check_device()) return r;
+  return launched(nf4::launch_embed(codes, scales, N, K, ids, T, out, dev_status,
+                                    (hipStream_t)stream));
+}
+
 void nf4_codebook(float out[16]) {
   if (!out) return;
   for (int i = 0; i < 16; ++i) std::memcpy(&out[i], &nf4::kLevelBits[i], 4);

@@ -1,0 +1,88 @@
+// embed.hip -- packed embedding rows: only the requested rows of an NF4 matrix
+// are decoded, into bf16 (deep-fold README, "Method": embeddings decode only
+// the requested rows; the result feeds the first linear layer as activations).
+//
+// out[t][k] = bf16(L[code(id,k)] * s(id, k/64)), id = ids[t], one rounding of
+// the exact product: p = the fp32 product, e = its exact error (one fma); p
+// decides the bf16 rounding except on an exact bf16 tie, where the sign of e
+// says on which side of it the exact product lies.  One thread writes 8
+// outputs (one 32-bit word of codes, 16 bytes of output).  An id outside
+// [0, N) gives a zero row and sets bit NF4_EMBED_BAD_ID of the status word.
+#include "nf4_device.h"
+#include "nf4_launch.h"
+
+namespace nf4 {
+
+// bf16 bits of the exact value p + e (p = fp32 rounding of a product, e its
+// exact rounding error); NaN gives the quiet NaN 0x7FC0.
+__device__ __forceinline__ uint32_t bf16_of_exact(float p, float e) {
+  const uint32_t b = __float_as_uint(p);
+  if ((b & 0x7F800000u) == 0x7F800000u) return (b & 0x007FFFFFu) ? 0x7FC0u : (b >> 16);
+  const uint32_t lo = b & 0xFFFFu;
+  const uint32_t r = b >> 16;
+  bool up;
+  if (lo != 0x8000u)
+    up = lo > 0x8000u;
+  else if (e != 0.0f)
+    up = (e > 0.0f) == (p > 0.0f);  // the exact value lies beyond the tie
+  else
+    up = (r & 1u) != 0u;            // exact tie: to even
+  return r + (up ? 1u : 0u);
+}
+
+__device__ __forceinline__ uint32_t embed_pair(uint32_t byte, float s) {
+  const float l0 = level_f32(byte & 15u), l1 = level_f32(byte >> 4);
+  const float p0 = __fmul_rn(l0, s), p1 = __fmul_rn(l1, s);
+  const float e0 = __fmaf_rn(l0, s, -p0), e1 = __fmaf_rn(l1, s, -p1);
+  return bf16_of_exact(p0, e0) | (bf16_of_exact(p1, e1) << 16);
+}
+
+constexpr int kEmbedThreads = 256;
+
+__global__ void __launch_bounds__(kEmbedThreads)
+    embed_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, int N,
+                 int K, const int64_t *__restrict__ ids, uint16_t *__restrict__ out,
+                 int32_t *status, int blocks_per_row) {
+  const int t = blockIdx.x / blocks_per_row;
+  const int c = (blockIdx.x - t * blocks_per_row) * kEmbedThreads + threadIdx.x;  // 8-value chunk
+  if (c >= (K >> 3)) return;
+  const int64_t id = ids[t];
+  uint4 o = make_uint4(0u, 0u, 0u, 0u);
+  if (id < 0 || id >= N) {
+    if (c == 0 && status) atomicOr(status, 1);
+  } else {
+    const uint32_t w =
+        *reinterpret_cast<const uint32_t *>(codes + id * (int64_t)(K >> 1) + (int64_t)c * 4);
+    const float s = f16_bits_to_f32(scales[id * (int64_t)(K >> 6) + (c >> 3)]);
+    o.x = embed_pair(w & 0xFFu, s);
+    o.y = embed_pair((w >> 8) & 0xFFu, s);
+    o.z = embed_pair((w >> 16) & 0xFFu, s);
+    o.w = embed_pair(w >> 24, s);
+  }
+  *reinterpret_cast<uint4 *>(out + (int64_t)t * K + (int64_t)c * 8) = o;
+}
+
+__global__ void clear_embed_status_kernel(int32_t *status) { *status = 0; }
+
+hipError_t launch_embed(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                        const int64_t *ids, int64_t T, uint16_t *out, int32_t *status,
+                        hipStream_t stream) {
+  if (status) {
+    hipLaunchKernelGGL(clear_embed_status_kernel, dim3(1), dim3(1), 0, stream, status);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (T == 0) return hipSuccess;
+  const int chunks = (int)(K >> 3);
+  const int bpr = (chunks + kEmbedThreads - 1) / kEmbedThreads;
+  hipLaunchKernelGGL(embed_kernel, dim3((unsigned)(T * bpr)), dim3(kEmbedThreads), 0, stream,
+                     codes, scales, (int)N, (int)K, ids, out, status, bpr);
+  return hipGetLastError();
+}
+
+int64_t embed_max_rows(int64_t K) {
+  const int64_t bpr = ((K >> 3) + kEmbedThreads - 1) / kEmbedThreads;
+  return ((int64_t(1) << 31) - 1) / bpr;
+}
+
+}  // namespace nf4

@@ -114,6 +114,28 @@ int nf4_gemv(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
 int nf4_gemm_smallm(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
                     const uint16_t *X, int64_t M, float *Y, void *stream);
 
+/* bit OR-ed into *dev_status by nf4_embed */
+#define NF4_EMBED_BAD_ID 1 /* an id outside [0, N): its output row is all +0 */
+
+/*
+ * nf4_embed -- packed embedding rows: decode only the rows ids[0..T-1] of the
+ * NF4 matrix (codes, scales) [N][K] into bf16:
+ *   out[t][k] = bf16(L[code(ids[t],k)] * s(ids[t],k/64)), the exact product
+ *   rounded once to nearest, ties to even (NaN scales give 0x7FC0).
+ * Source: deep-fold README, "Method" (embeddings decode only the requested
+ * rows; the rows then feed the first linear layer as bf16 activations).
+ *  - ids: device int64 [T]; repeated ids are allowed.  An id outside [0, N)
+ *    writes a zero row and OR-s NF4_EMBED_BAD_ID into *dev_status (device
+ *    int32, may be NULL; if given, the call first clears it to 0 on the stream).
+ *  - out: device bf16 bits [T][K].  T = 0 is valid and writes nothing.
+ * Alignment: codes 4 bytes, scales 2, ids 8, out 16.  Errors: NF4_EINVAL for a
+ * null pointer or T < 0, NF4_ERANGE if T is too large for one launch
+ * (> 2^31 / ceil(K / 2048)), plus the shape rules of every call.
+ */
+int nf4_embed(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+              const int64_t *ids, int64_t T, uint16_t *out, int32_t *dev_status,
+              void *stream);
+
 /* The 16 NF4 levels L[0..15] (fp32) this library decodes with.  Host only. */
 void nf4_codebook(float out[16]);
 

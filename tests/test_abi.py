@@ -32,14 +32,15 @@ def lib():
     L.nf4_unpack.argtypes = [vp, vp, i64, i64, vp, vp]
     L.nf4_gemv.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     L.nf4_gemm_smallm.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp]
+    L.nf4_embed.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, vp]
     L.nf4_strerror.restype = ctypes.c_char_p
     return L
 
 
 def test_header_declares_the_boundary():
     names = _declared()
-    for required in ("nf4_pack", "nf4_unpack", "nf4_gemv", "nf4_gemm_smallm", "nf4_codebook",
-                     "nf4_strerror"):
+    for required in ("nf4_pack", "nf4_unpack", "nf4_gemv", "nf4_gemm_smallm", "nf4_embed",
+                     "nf4_codebook", "nf4_strerror"):
         assert required in names
 
 
@@ -71,6 +72,7 @@ def test_shape_validation(lib, N, K, expect):
     assert lib.nf4_gemm_smallm(P, P, N, K, P, 4, P, NULL) == expect
     assert lib.nf4_pack(P, N, K, P, P, NULL, NULL) == expect
     assert lib.nf4_unpack(P, P, N, K, P, NULL) == expect
+    assert lib.nf4_embed(P, P, N, K, P, 4, P, NULL, NULL) == expect
 
 
 def test_null_pointers(lib):
@@ -98,3 +100,13 @@ def test_alignment(lib):
 def test_strerror(lib):
     for code in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(lib.nf4_strerror(code), bytes)
+
+
+def test_embed_validation(lib):
+    assert lib.nf4_embed(NULL, P, 4, 64, P, 1, P, NULL, NULL) == EINVAL
+    assert lib.nf4_embed(P, P, 4, 64, NULL, 1, P, NULL, NULL) == EINVAL   # ids
+    assert lib.nf4_embed(P, P, 4, 64, P, 1, NULL, NULL, NULL) == EINVAL   # out
+    assert lib.nf4_embed(P, P, 4, 64, P, -1, P, NULL, NULL) == EINVAL     # T < 0
+    assert lib.nf4_embed(P, P, 4, 64, P, 1, P_ODD, NULL, NULL) == EALIGN  # out needs 16 B
+    assert lib.nf4_embed(P, P, 4, 64, ctypes.c_void_p(0x100004), 1, P, NULL, NULL) == EALIGN
+    assert lib.nf4_embed(P, P, 4, 64, P, 2 ** 31, P, NULL, NULL) == ERANGE
