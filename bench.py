@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out", default="", help="also append the JSON line to this file")
+    ap.add_argument("--embed", type=int, default=0, metavar="T",
+                    help="instead of the layer set: packed-embedding rows, T token ids per "
+                         "call from a 32000 x 4096 (Llama-2) vocabulary matrix")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times): the reference "
                          "kernel whose FETCH_SIZE / WRITE_SIZE counters calibrate the HBM "
@@ -114,6 +117,86 @@ def cpu_baseline(set_, M, seconds):
             "host": platform.processor() or platform.machine()}
 
 
+EMBED_METRIC = "NF4 packed-embedding rows (decode only the requested rows) effective GB/s"
+
+
+def bench_embed(args, torch, dev):
+    """Packed embedding rows: T ids per call into bf16 rows of a Llama-2-sized
+    vocabulary matrix; bytes per call = the T packed rows (codes + scales), the
+    ids and the bf16 output."""
+    import dequant_gemv_nf4_amd as nf4
+    import oracle
+    import workloads as wl
+    N, K, T = 32000, 4096, args.embed
+    W = wl.weights(N, K, 0.02, wl.seed_for("embed", 0, "tok", "W"), dev)
+    codes, scales = nf4.pack(W)
+    del W
+    rng = np.random.default_rng(17)
+    R = 64  # distinct id sets, rotated through
+    idsets = [torch.from_numpy(rng.integers(0, N, T).astype(np.int64)).to(dev) for _ in range(R)]
+    outs = [torch.empty((T, K), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+    def launch(i):
+        nf4.nf4_embed(codes, scales, K, idsets[i % R], outs[i % R])
+    for i in range(R):
+        launch(i)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        launch(0)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(R):
+            launch(i)
+    for _ in range(max(1, args.warmup)):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    us_per_call = ms * 1e3 / (args.steps * R)
+    nbytes = T * (K // 2 + 2 * (K // 64)) + 8 * T + 2 * T * K
+    gbs = nbytes / us_per_call / 1e3
+    log(f"embed T={T}: {us_per_call:.2f} us per call, {gbs:.0f} GB/s")
+    out = {"metric": EMBED_METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "nf4-w/bf16-out", "data": "synthetic",
+           "config": {"workload": f"packed embedding rows, {N}x{K} vocabulary, T={T} ids per call",
+                      "calls_per_step": R, "timing": "hip-graph replay"},
+           "us_per_call": round(us_per_call, 3),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                        "kernel": "embed_kernel", "bytes_per_launch": nbytes,
+                        "us_per_launch": round(us_per_call, 3)}}
+    if not args.no_cpu_baseline:
+        ids = idsets[0].cpu().numpy()
+        rows = np.unique(ids)
+        p = codes[torch.from_numpy(rows).to(dev)].cpu().numpy()
+        sc = scales[torch.from_numpy(rows).to(dev)].cpu().numpy().view(np.uint16)
+        local = np.searchsorted(rows, ids)
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 10.0):
+            oracle.embed(p, sc, local)
+            reps += 1
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{reps} calls of T={T} rows in {dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(json.dumps(out) + "\n")
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -132,6 +215,8 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.embed:
+        return bench_embed(args, torch, dev)
     if args.copy_calibration:
         n = args.copy_calibration << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
