@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     MAX_M,
     EMBED_BAD_ID,
     NF4Error,
+    Ring,
     PACK_NONFINITE,
     PACK_SCALE_OVERFLOW,
     embed,
@@ -30,5 +31,6 @@ from ._lib import (  # noqa: F401
     nf4_pack,
     nf4_unpack,
     pack,
+    ring_slot_bytes,
     unpack,
 )

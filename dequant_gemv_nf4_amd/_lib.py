@@ -46,6 +46,13 @@ def _load():
     L.nf4_gemv.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     L.nf4_gemm_smallm.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp]
     L.nf4_embed.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, vp]
+    L.nf4_ring_create.argtypes = [ctypes.POINTER(ctypes.c_void_p), vp, vp, i64, vp, vp]
+    L.nf4_ring_gemm.argtypes = [vp, vp, vp, i64, i64, vp, i64, vp]
+    L.nf4_ring_destroy.argtypes = [vp]
+    L.nf4_ring_slot_bytes.argtypes = [i64, i64]
+    L.nf4_ring_slot_bytes.restype = ctypes.c_int64
+    for f in (L.nf4_ring_create, L.nf4_ring_gemm, L.nf4_ring_destroy):
+        f.restype = ctypes.c_int
     for f in (L.nf4_pack, L.nf4_unpack, L.nf4_gemv, L.nf4_gemm_smallm, L.nf4_embed):
         f.restype = ctypes.c_int
     L.nf4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
@@ -168,6 +175,61 @@ def nf4_embed(codes, scales, K, ids, out, dev_status=None, stream=None):
         _check("nf4_embed", _load().nf4_embed(_ptr(codes), _ptr(scales), N, K, _ptr(ids), T,
                                               _ptr(out), _ptr(dev_status),
                                               _stream(codes.device, stream)))
+
+
+def ring_slot_bytes(N, K):
+    """Device bytes one CopyRing slot needs for an N x K packed matrix."""
+    return int(_load().nf4_ring_slot_bytes(N, K))
+
+
+class Ring:
+    """CopyRing (nf4_ring_*): products over packed matrices in pinned host memory,
+    streamed through two device slots of `slot_bytes` each.  Copies run on their
+    own stream, products on `compute_stream` (default: the current stream)."""
+
+    def __init__(self, slot_bytes, device, compute_stream=None, copy_stream=None):
+        self.device = torch.device(device)
+        self.slots = [torch.empty(slot_bytes, dtype=torch.uint8, device=self.device)
+                      for _ in range(2)]
+        self.compute_stream = compute_stream or torch.cuda.current_stream(self.device)
+        self.copy_stream = copy_stream or torch.cuda.Stream(self.device)
+        self._ring = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            _check("nf4_ring_create", _load().nf4_ring_create(
+                ctypes.byref(self._ring), _ptr(self.slots[0]), _ptr(self.slots[1]), slot_bytes,
+                ctypes.c_void_p(self.compute_stream.cuda_stream),
+                ctypes.c_void_p(self.copy_stream.cuda_stream)))
+        self._keep = []  # host buffers of enqueued copies, held until close()
+
+    def gemm(self, host_codes, host_scales, X, Y):
+        """Y [M][N] fp32 = X bf16 [M][K] . dequant(host_codes, host_scales)^T."""
+        for t, n in ((host_codes, "host_codes"), (host_scales, "host_scales")):
+            if t.device.type != "cpu" or not t.is_pinned() or not t.is_contiguous():
+                raise ValueError(f"{n} must be a contiguous pinned host tensor")
+        _need(X, "X", _BF16, (1, 2))
+        _need(Y, "Y", (torch.float32,))
+        M, K = (1, X.shape[0]) if X.dim() == 1 else X.shape
+        N = _nk(host_codes, host_scales, K)
+        if Y.numel() != M * N:
+            raise ValueError("Y must have M*N elements")
+        self._keep.append((host_codes, host_scales))
+        with torch.cuda.device(self.device):
+            _check("nf4_ring_gemm", _load().nf4_ring_gemm(
+                self._ring, _ptr(host_codes), _ptr(host_scales), N, K, _ptr(X), M, _ptr(Y)))
+
+    def close(self):
+        if self._ring:
+            with torch.cuda.device(self.device):
+                st = _load().nf4_ring_destroy(self._ring)
+            self._ring = ctypes.c_void_p()
+            self._keep.clear()
+            _check("nf4_ring_destroy", st)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def nf4_codebook():

@@ -43,6 +43,10 @@ int launched(hipError_t e) { return e == hipSuccess ? NF4_OK : NF4_ELAUNCH; }
 
 }  // namespace
 
+namespace nf4 {
+int device_status() { return check_device(); }
+}  // namespace nf4
+
 extern "C" {
 
 int nf4_pack(const float *W, int64_t N, int64_t K, uint8_t *codes, uint16_t *scales,

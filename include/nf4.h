@@ -136,6 +136,43 @@ int nf4_embed(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K
               const int64_t *ids, int64_t T, uint16_t *out, int32_t *dev_status,
               void *stream);
 
+/*
+ * CopyRing -- products over packed matrices held in pinned host memory,
+ * streamed through two reusable device slots.  Source: deep-fold README,
+ * "Method" (models exceeding the GPU budget: selected packed matrices stream
+ * from pinned host memory through two reusable GPU slots into the same kernel).
+ *
+ * nf4_ring_create: slot0 / slot1 are caller-owned device buffers of slot_bytes
+ * each (256-byte aligned); compute_stream and copy_stream are two hipStreams
+ * (void*; NULL = null stream, but two distinct streams are needed for overlap).
+ * The ring object and its four HIP events are created here and released by
+ * nf4_ring_destroy, which first waits until the ring's last product is done.
+ * The ring keeps the slot pointers and streams until then; a ring is used by
+ * one host thread at a time.
+ *
+ * nf4_ring_gemm: Y[m][n] = sum_k L[code(n,k)] s(n,k/64) X[m][k] exactly as
+ * nf4_gemm_smallm (same kernels, same bits), with codes [N][K/2] and scales
+ * [N][K/64] in pinned host memory (allocated with hipHostMalloc or an equivalent;
+ * a pageable pointer is rejected with NF4_EINVAL).  The call takes the next slot,
+ * enqueues on the copy stream a wait for the slot's previous product, the copy
+ * of codes (slot offset 0) and scales (offset rounded up to 256 bytes), and on the
+ * compute stream a wait for that copy and the product; it returns at once.
+ * X and Y are device memory, read / written on the compute stream.  The host
+ * buffers must stay valid until the copy has run.  Errors: NF4_ERANGE if the
+ * matrix does not fit a slot (see nf4_ring_slot_bytes) or M is outside [1, 32];
+ * NF4_EDEVICE if the current device is not the ring's; the shape and alignment
+ * rules of nf4_gemm_smallm otherwise.
+ *
+ * nf4_ring_slot_bytes: bytes a slot needs for an N x K matrix (-1 if invalid).
+ */
+typedef struct nf4_ring nf4_ring;
+int nf4_ring_create(nf4_ring **ring, void *slot0, void *slot1, int64_t slot_bytes,
+                    void *compute_stream, void *copy_stream);
+int nf4_ring_gemm(nf4_ring *ring, const uint8_t *host_codes, const uint16_t *host_scales,
+                  int64_t N, int64_t K, const uint16_t *X, int64_t M, float *Y);
+int64_t nf4_ring_slot_bytes(int64_t N, int64_t K);
+int nf4_ring_destroy(nf4_ring *ring);
+
 /* The 16 NF4 levels L[0..15] (fp32) this library decodes with.  Host only. */
 void nf4_codebook(float out[16]);
 

@@ -33,6 +33,11 @@ def lib():
     L.nf4_gemv.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     L.nf4_gemm_smallm.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp]
     L.nf4_embed.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, vp]
+    L.nf4_ring_create.argtypes = [ctypes.POINTER(ctypes.c_void_p), vp, vp, i64, vp, vp]
+    L.nf4_ring_gemm.argtypes = [vp, vp, vp, i64, i64, vp, i64, vp]
+    L.nf4_ring_destroy.argtypes = [vp]
+    L.nf4_ring_slot_bytes.argtypes = [i64, i64]
+    L.nf4_ring_slot_bytes.restype = ctypes.c_int64
     L.nf4_strerror.restype = ctypes.c_char_p
     return L
 
@@ -40,6 +45,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = _declared()
     for required in ("nf4_pack", "nf4_unpack", "nf4_gemv", "nf4_gemm_smallm", "nf4_embed",
+                     "nf4_ring_create", "nf4_ring_gemm", "nf4_ring_slot_bytes", "nf4_ring_destroy",
                      "nf4_codebook", "nf4_strerror"):
         assert required in names
 
@@ -110,3 +116,18 @@ def test_embed_validation(lib):
     assert lib.nf4_embed(P, P, 4, 64, P, 1, P_ODD, NULL, NULL) == EALIGN  # out needs 16 B
     assert lib.nf4_embed(P, P, 4, 64, ctypes.c_void_p(0x100004), 1, P, NULL, NULL) == EALIGN
     assert lib.nf4_embed(P, P, 4, 64, P, 2 ** 31, P, NULL, NULL) == ERANGE
+
+
+def test_ring_validation_without_a_device(lib):
+    out = ctypes.c_void_p()
+    assert lib.nf4_ring_create(None, P, P, 1024, NULL, NULL) == EINVAL
+    assert lib.nf4_ring_create(ctypes.byref(out), NULL, P, 1024, NULL, NULL) == EINVAL
+    assert lib.nf4_ring_create(ctypes.byref(out), P, P, 0, NULL, NULL) == EINVAL
+    assert lib.nf4_ring_create(ctypes.byref(out), ctypes.c_void_p(0x100010), P, 1024, NULL,
+                               NULL) == EALIGN
+    assert lib.nf4_ring_gemm(NULL, P, P, 4, 64, P, 1, P) == EINVAL
+    assert lib.nf4_ring_destroy(NULL) == EINVAL
+    # codes at offset 0, scales on the next 256-byte boundary
+    assert lib.nf4_ring_slot_bytes(4, 64) == 256 + 4 * 2
+    assert lib.nf4_ring_slot_bytes(4096, 4096) == 4096 * 2048 + 4096 * 64 * 2
+    assert lib.nf4_ring_slot_bytes(4, 65) == -1
