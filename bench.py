@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--embed", type=int, default=0, metavar="T",
                     help="instead of the layer set: packed-embedding rows, T token ids per "
                          "call from a 32000 x 4096 (Llama-2) vocabulary matrix")
+    ap.add_argument("--copyring", action="store_true",
+                    help="instead of resident weights: stream the layer set's packed matrices "
+                         "from pinned host memory through two device slots (CopyRing)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times): the reference "
                          "kernel whose FETCH_SIZE / WRITE_SIZE counters calibrate the HBM "
@@ -197,6 +200,97 @@ def bench_embed(args, torch, dev):
             f.write(json.dumps(out) + "\n")
 
 
+RING_METRIC = "NF4 GEMV over packed weights streamed from pinned host memory (CopyRing), GB/s"
+HOST_LINK_GBS = 64.0  # PCIe 5.0 x16, one direction, published
+
+
+def bench_copyring(args, torch, dev):
+    """CopyRing: every product of the layer set reads its packed matrix from
+    pinned host memory through two device slots; a step is one sweep of all
+    layers.  value = algorithmic bytes per step / step time (the packed bytes
+    cross the host link once per step)."""
+    import dequant_gemv_nf4_amd as nf4
+    import workloads as wl
+    set_ = wl.ALL_SETS[args.set]
+    M = args.m
+    L = args.layers or min(set_.layers, 8)
+    groups_ = wl.launch_groups(set_, fused=not args.unfused)
+    items = []
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    for layer in range(L):
+        for name, projs in groups_:
+            K = projs[0][2]
+            N = sum(n for _, n, _ in projs)
+            codes, scales = nf4.empty_packed(N, K, dev)
+            r0 = 0
+            for proj, n, _ in projs:
+                W = wl.weights(n, K, set_.sigma, wl.seed_for(set_.name, layer, proj, "W"), dev)
+                nf4.nf4_pack(W, codes[r0:r0 + n], scales[r0:r0 + n], status)
+                del W
+                r0 += n
+            hc = torch.empty(codes.shape, dtype=codes.dtype, pin_memory=True)
+            hs = torch.empty(scales.shape, dtype=scales.dtype, pin_memory=True)
+            hc.copy_(codes)
+            hs.copy_(scales)
+            del codes, scales
+            X = wl.activations(M, K, wl.seed_for(set_.name, layer, name, "x"), dev)
+            Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            items.append((name, N, K, hc, hs, X, Y))
+    torch.cuda.synchronize()
+    slot = max(nf4.ring_slot_bytes(N, K) for _, N, K, *_ in items)
+    ring = nf4.Ring(slot, dev)
+    step_bytes = sum(wl.algorithmic_bytes(N, K, M) for _, N, K, *_ in items)
+    packed = sum(hc.numel() + 2 * hs.numel() for _, _, _, hc, hs, _, _ in items)
+    log(f"copyring: {set_.name}, {L} layers, {packed / 1e9:.2f} GB pinned, slots 2 x {slot / 1e6:.1f} MB")
+
+    def sweep():
+        for _, N, K, hc, hs, X, Y in items:
+            ring.gemm(hc, hs, X, Y)
+    for _ in range(args.warmup):
+        sweep()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    steps = max(1, min(args.steps, 5))
+    e0.record()
+    for _ in range(steps):
+        sweep()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    value = step_bytes / (ms / 1e3) / 1e9
+    # the same bytes copied with nothing else running: the host link's rate here
+    slots = ring.slots
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for i, (_, _, _, hc, hs, _, _) in enumerate(items):
+        slots[i % 2][:hc.numel()].copy_(hc.view(-1), non_blocking=True)
+        slots[i % 2][hc.numel():hc.numel() + 2 * hs.numel()].view(torch.int16).copy_(
+            hs.view(-1), non_blocking=True)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = packed / (c0.elapsed_time(c1) / 1e3) / 1e9
+    ring.close()
+    log(f"copyring: {ms * 1e3:.1f} us per step, {value:.1f} GB/s; plain H2D copy of the same "
+        f"bytes {copy_gbs:.1f} GB/s")
+    out = {"metric": RING_METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+           "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "nf4-w/bf16-x/f16-dot/fp32-acc", "data": "synthetic",
+           "config": {"workload": f"{set_.name} layer set through CopyRing, M={M}", "layers": L,
+                      "packed_gb": round(packed / 1e9, 3), "slot_mb": round(slot / 1e6, 2),
+                      "timing": "eager (two streams)"},
+           "h2d_copy_gbs": round(copy_gbs, 2),
+           "roofline": {"bound": "host-link", "achieved": round(value, 1), "peak": HOST_LINK_GBS,
+                        "unit": "GB/s", "frac": round(value / HOST_LINK_GBS, 4), "traffic": None,
+                        "kernel": "CopyRing (H2D copy + gemv_valu_kernel)"}}
+    print(json.dumps(out), flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(json.dumps(out) + "\n")
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -217,6 +311,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.embed:
         return bench_embed(args, torch, dev)
+    if args.copyring:
+        return bench_copyring(args, torch, dev)
     if args.copy_calibration:
         n = args.copy_calibration << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)

@@ -2,10 +2,15 @@
 
     python -m dequant_gemv_nf4_amd.rocpd_summary trace  <results.db> [name-filter]
     python -m dequant_gemv_nf4_amd.rocpd_summary pmc    <results.db> [name-filter]
+    python -m dequant_gemv_nf4_amd.rocpd_summary copies <results.db> [name-filter]
 
 `trace` groups dispatches by (kernel, grid, workgroup) and prints count, mean,
 median, p10 and p90 duration.  `pmc` prints the mean of every collected counter
-per (kernel, grid).  Both read only what rocprofv3 wrote.
+per (kernel, grid).  `copies` groups memory copies by direction and size (count,
+mean duration, GB/s), then reports how the copies and the filtered kernels
+overlap in time: the busy time of the copy engine over the span from the first
+to the last copy, and how many kernels ran while a copy was in flight.  All
+read only what rocprofv3 wrote.
 """
 import collections
 import sqlite3
@@ -49,7 +54,42 @@ def pmc(path, filt=""):
     return out
 
 
+def copies(path, filt=""):
+    db = sqlite3.connect(path)
+    rows = db.execute("select name, size, start, end from memory_copies order by start").fetchall()
+    kern = [(s, e) for name, s, e in db.execute("select name, start, end from kernels")
+            if not filt or filt in name]
+    groups = collections.OrderedDict()
+    for name, size, s, e in rows:
+        groups.setdefault((name, size), []).append((e - s) / 1e3)
+    out = []
+    for (name, size), d in groups.items():
+        m = statistics.mean(d)
+        out.append(f"{name:32s} size {size:11d} n {len(d):4d} mean {m:9.2f} us  "
+                   f"{size / m / 1e3:7.2f} GB/s")
+    if rows:
+        t0, t1 = rows[0][2], max(e for *_, e in rows)
+        busy, cur_s, cur_e = 0, None, None
+        for *_, s, e in rows:  # union of copy intervals
+            if cur_e is None or s > cur_e:
+                if cur_e is not None:
+                    busy += cur_e - cur_s
+                cur_s, cur_e = s, e
+            else:
+                cur_e = max(cur_e, e)
+        busy += cur_e - cur_s
+        inside = [k for k in kern if k[0] >= t0 and k[1] <= t1]
+        during = sum(1 for ks, ke in inside
+                     if any(s < ke and e > ks for *_, s, e in rows))
+        moved = sum(size for _, size, _, _ in rows)
+        out.append(f"copies span {(t1 - t0) / 1e3:.1f} us, copy engine busy {busy / (t1 - t0):.1%} "
+                   f"of it, {moved / ((t1 - t0) / 1e3) / 1e3:.2f} GB/s over the span; "
+                   f"{during} of {len(inside)} kernels in the span ran while a copy was in flight")
+    return out
+
+
 if __name__ == "__main__":
     mode, path = sys.argv[1], sys.argv[2]
     filt = sys.argv[3] if len(sys.argv) > 3 else ""
-    print("\n".join(trace(path, filt) if mode == "trace" else pmc(path, filt)))
+    fn = {"trace": trace, "pmc": pmc, "copies": copies}[mode]
+    print("\n".join(fn(path, filt)))
