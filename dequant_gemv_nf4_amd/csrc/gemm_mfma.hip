@@ -259,6 +259,184 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pair-step variant (an even number of groups per row and 4-byte aligned
+// scales, which covers every model shape): a step is a pair of groups (128 k,
+// 64 code bytes per row).  A lane loads 16 contiguous code bytes of its row --
+// lane-group g takes bytes 16g .. 16g+15 of the pair, so one wave instruction
+// reads 64 contiguous bytes of each of 16 rows -- and one 32-bit word holding
+// both scales of the pair.  Lane-groups 0/1 then hold bytes of the first group
+// and 2/3 of the second; one v_permlane32_swap per half (lanes l <-> l + 32)
+// leaves every lane with 8 bytes of each group: byte offset pi(g) = 0, 16, 8,
+// 24 for g = 0..3 within the group, the same in both groups, so each MFMA still
+// covers one group and its tile is scaled by that group's scale.  Every load is
+// a buffer load whose per-lane offset is fixed and whose step offset is a
+// scalar: no vector address arithmetic per step.
+// ---------------------------------------------------------------------------
+template <int MT, int TB, int D>
+__global__ void __launch_bounds__(kThreads)
+    gemm_mfma_pair_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
+                          const uint16_t *__restrict__ X, float *__restrict__ Y, int N, int K,
+                          int M) {
+  constexpr int kRedWords = kWaves * TB * MT * 4 * 64;
+  constexpr int kLdsWords = kRedWords > kLutWords ? kRedWords : kLutWords;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsWords];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, lg = lane >> 4;
+  const int NG = K >> 6;
+  const int NP = NG >> 1;  // pairs per row
+  const int NT = (N + 15) >> 4;
+  const int t0 = blockIdx.x * TB;
+  const int nsteps = wave < NP ? (NP - 1 - wave) / kWaves + 1 : 0;
+
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(codes), 0, (int)((int64_t)N * (K >> 1)), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(scales), 0, (int)((int64_t)N * NG * 2), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(X), 0, M * K * 2, kBufferWord3);
+
+  // fixed per-lane byte offsets; tiles past the end re-read the first tile,
+  // columns past N re-read row N-1
+  int cvo[TB], svo[TB];
+#pragma unroll
+  for (int j = 0; j < TB; ++j) {
+    const int t = (t0 + j < NT) ? t0 + j : t0;
+    const int n = min(16 * t + col, N - 1);
+    cvo[j] = n * (K >> 1) + 16 * lg;
+    svo[j] = n * NG * 2;
+  }
+  // activations of lane-group g after the swap: k = 128 p + 64 q + 2 pi(g) + 8 h + e
+  const int pi2 = 2 * ((lg & 1) * 16 + (lg >> 1) * 8);  // 2 pi(g): 0, 32, 16, 48
+  int xvo[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) xvo[mt] = (min(16 * mt + col, M - 1) * K + pi2) * 2;
+
+  u32x4_t rc[D][TB];
+  uint32_t rs[D][TB];
+  u32x4_t ra[D][MT][4];  // [group q][half h] -> index 2q + h
+
+  auto load = [&](auto slot, int i) __attribute__((always_inline)) {
+    constexpr int d = decltype(slot)::value;
+    const int p = __builtin_amdgcn_readfirstlane(min(wave + kWaves * i, NP - 1));
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      rc[d][j] = __builtin_amdgcn_raw_buffer_load_b128(crs, cvo[j], 64 * p, kLoadStream);
+      rs[d][j] = __builtin_amdgcn_raw_buffer_load_b32(srs, svo[j], 4 * p, 0);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          ra[d][mt][2 * q + h] =
+              __builtin_amdgcn_raw_buffer_load_b128(xrs, xvo[mt] + 128 * q + 16 * h, 256 * p, 0);
+  };
+
+  f32x4_t acc[TB][MT];
+#pragma unroll
+  for (int j = 0; j < TB; ++j)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[j][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const uint32_t laneoff = 8u * (lane & 31);
+  auto compute = [&](auto slot) __attribute__((always_inline)) {
+    constexpr int d = decltype(slot)::value;
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      // lanes l and l + 32 trade halves: afterwards words 0, 1 hold the first
+      // group's bytes and words 2, 3 the second's
+      const u32x4_t c = rc[d][j];
+      const auto s02 = __builtin_amdgcn_permlane32_swap(c[0], c[2], false, false);
+      const auto s13 = __builtin_amdgcn_permlane32_swap(c[1], c[3], false, false);
+      const uint32_t wq[2][2] = {{s02[0], s13[0]}, {s02[1], s13[1]}};
+      const uint32_t sw = rs[d][j];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        f32x4_t g[MT];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t w = wq[q][h];
+          u32x4_t bh, bl;
+          u32x2_t e;
+          e = lds_load_u64(lds, split_addr<0>(w, laneoff)); bh[0] = e[0]; bl[0] = e[1];
+          e = lds_load_u64(lds, split_addr<1>(w, laneoff)); bh[1] = e[0]; bl[1] = e[1];
+          e = lds_load_u64(lds, split_addr<2>(w, laneoff)); bh[2] = e[0]; bl[2] = e[1];
+          e = lds_load_u64(lds, split_addr<3>(w, laneoff)); bh[3] = e[0]; bl[3] = e[1];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const u32x4_t a = ra[d][mt][2 * q + h];
+            g[mt] = mfma_bf16(a, bh, h == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : g[mt]);
+            g[mt] = mfma_bf16(a, bl, g[mt]);
+          }
+        }
+        const float sc = f16_bits_to_f32(q == 0 ? (sw & 0xffffu) : (sw >> 16));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[j][mt][r] = fmaf(g[mt][r], sc, acc[j][mt][r]);
+      }
+    }
+  };
+
+  // (slots issued in the loop's order, so the waits agree on both paths into it)
+  for_slots(
+      [&](auto slot) __attribute__((always_inline)) {
+        load(slot, decltype(slot)::value);
+        __builtin_amdgcn_sched_barrier(0);
+      },
+      std::make_integer_sequence<int, D>{});
+  build_split_lut(lds, lane, wave);
+  __syncthreads();
+
+  // whole rounds without branches, then the last partial round
+  int base = 0;
+  for (; base + D <= nsteps; base += D) {
+    for_slots(
+        [&](auto slot) __attribute__((always_inline)) {
+          constexpr int d = decltype(slot)::value;
+          compute(slot);
+          load(slot, base + d + D);
+          // keep each slot's refill right after its use (the scheduler would
+          // otherwise sink all refills to the end of the round)
+          __builtin_amdgcn_sched_barrier(0);
+        },
+        std::make_integer_sequence<int, D>{});
+  }
+  for_slots(
+      [&](auto slot) __attribute__((always_inline)) {
+        constexpr int d = decltype(slot)::value;
+        if (base + d < nsteps) compute(slot);
+      },
+      std::make_integer_sequence<int, D>{});
+
+  __syncthreads();  // the table is no longer read
+  float *red = reinterpret_cast<float *>(lds);
+#pragma unroll
+  for (int j = 0; j < TB; ++j)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        red[(((wave * TB + j) * MT + mt) * 4 + r) * 64 + lane] = acc[j][mt][r];
+  __syncthreads();
+  constexpr int kOut = TB * MT * 256;
+  for (int o = tid; o < kOut; o += kThreads) {
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) sum += red[w * kOut + o];
+    const int ln = o & 63, r = (o >> 6) & 3, tm = o >> 8;
+    const int mt = tm % MT, j = tm / MT;
+    const int m = 16 * mt + 4 * (ln >> 4) + r;
+    const int n = 16 * (t0 + j) + (ln & 15);
+    if (t0 + j < NT && m < M && n < N) Y[(int64_t)m * N + n] = sum;
+  }
+}
+
 namespace {
 
 constexpr int kCUs = 256;
@@ -273,6 +451,32 @@ hipError_t go(const uint8_t *codes, const uint16_t *scales, int N, int K, const 
   hipLaunchKernelGGL((gemm_mfma_kernel<MT, TB, D>), dim3(blocks), dim3(kThreads), 0, stream, codes,
                      scales, X, Y, N, K, M);
   return hipGetLastError();
+}
+
+template <int MT, int TB>
+hipError_t go_pair(const uint8_t *codes, const uint16_t *scales, int N, int K, const uint16_t *X,
+                   int M, float *Y, hipStream_t stream) {
+  constexpr int D = 2;  // pairs in flight per wave
+  const int tiles = (N + 15) / 16;
+  const int blocks = (tiles + TB - 1) / TB;
+  hipLaunchKernelGGL((gemm_mfma_pair_kernel<MT, TB, D>), dim3(blocks), dim3(kThreads), 0, stream,
+                     codes, scales, X, Y, N, K, M);
+  return hipGetLastError();
+}
+
+template <int MT>
+hipError_t go_pair_tb(int TB, const uint8_t *codes, const uint16_t *scales, int N, int K,
+                      const uint16_t *X, int M, float *Y, hipStream_t s) {
+  switch (TB) {
+    case 1: return go_pair<MT, 1>(codes, scales, N, K, X, M, Y, s);
+    case 2: return go_pair<MT, 2>(codes, scales, N, K, X, M, Y, s);
+    case 3: return go_pair<MT, 3>(codes, scales, N, K, X, M, Y, s);
+    case 4: return go_pair<MT, 4>(codes, scales, N, K, X, M, Y, s);
+    case 5: return go_pair<MT, 5>(codes, scales, N, K, X, M, Y, s);
+    case 6: return go_pair<MT, 6>(codes, scales, N, K, X, M, Y, s);
+    case 7: return go_pair<MT, 7>(codes, scales, N, K, X, M, Y, s);
+    default: return go_pair<MT, 8>(codes, scales, N, K, X, M, Y, s);
+  }
 }
 
 template <int MT>
@@ -300,6 +504,13 @@ hipError_t launch_gemm_mfma(const uint8_t *codes, const uint16_t *scales, int64_
   // (past that, workgroups run in rounds)
   const int tiles = (n + 15) / 16;
   const int TB = std::min((tiles + kCUs - 1) / kCUs, 8);
+  // pair steps need an even group count and 4-byte aligned scales (every model
+  // shape); otherwise one group per step
+  const bool pair = ((k >> 6) % 2 == 0) && ((reinterpret_cast<uintptr_t>(scales) & 3) == 0);
+  if (pair) {
+    if (M <= 16) return go_pair_tb<1>(TB, codes, scales, n, k, X, M, Y, stream);
+    return go_pair_tb<2>(TB, codes, scales, n, k, X, M, Y, stream);
+  }
   if (M <= 16) return go_tb<1>(TB, codes, scales, n, k, X, M, Y, stream);
   return go_tb<2>(TB, codes, scales, n, k, X, M, Y, stream);
 }

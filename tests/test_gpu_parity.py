@@ -159,7 +159,8 @@ def test_gemm_smallm_m_sweep(nf4, M):
 
 
 @pytest.mark.parametrize("M,N,K", [(4, 33, 14336), (8, 100, 4096), (32, 48, 14336),
-                                   (5, 20, 20480), (8, 17, 64), (32, 1, 128), (16, 4111, 192)])
+                                   (5, 20, 20480), (8, 17, 64), (32, 1, 128), (16, 4111, 192),
+                                   (32, 40, 320), (24, 300, 2048)])
 def test_gemm_smallm_shapes(nf4, M, N, K):
     _product_case(nf4, M, N, K, seed=3)
 
@@ -281,3 +282,21 @@ def test_pack_into_row_slices_of_a_fused_matrix(nf4):
     torch.cuda.synchronize()
     yr, A = oracle.gemm(ref_p, ref_s, wl.bf16_bits(x))
     _check_product(y.reshape(1, -1), yr, A, "fused q|k|v")
+
+
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_products_with_scales_only_2_byte_aligned(nf4, M):
+    """Scales at an address that is 2 but not 4 bytes aligned (allowed by the ABI)
+    take the 16-bit scale paths; results match the oracle."""
+    N, K = 96, 1024
+    W = wl.weights(N, K, 0.02, seed=60 + M, device=DEV)
+    codes, scales = _pack_gpu(nf4, W)[:2]
+    buf = torch.zeros(N * (K // 64) + 1, dtype=torch.int16, device=DEV)
+    buf[1:].copy_(scales.view(-1))
+    sc = buf[1:].view(N, K // 64)
+    assert sc.data_ptr() % 4 == 2
+    X = wl.activations(M, K, seed=70 + M, device=DEV)
+    Y = nf4.gemv(codes, sc, X[0]) if M == 1 else nf4.gemm(codes, sc, X)
+    torch.cuda.synchronize()
+    Yr, A = oracle.gemm(codes.cpu().numpy(), _u16(scales), wl.bf16_bits(X))
+    _check_product(Y.reshape(M, N), Yr, A, f"unaligned scales M={M}")
