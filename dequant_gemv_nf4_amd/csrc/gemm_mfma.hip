@@ -456,7 +456,7 @@ hipError_t go(const uint8_t *codes, const uint16_t *scales, int N, int K, const 
 template <int MT, int TB>
 hipError_t go_pair(const uint8_t *codes, const uint16_t *scales, int N, int K, const uint16_t *X,
                    int M, float *Y, hipStream_t stream) {
-  constexpr int D = 2;  // pairs in flight per wave
+  constexpr int D = 1;  // pairs in flight per wave (measured: deeper rings run slower)
   const int tiles = (N + 15) / 16;
   const int blocks = (tiles + TB - 1) / TB;
   hipLaunchKernelGGL((gemm_mfma_pair_kernel<MT, TB, D>), dim3(blocks), dim3(kThreads), 0, stream,
@@ -473,7 +473,8 @@ hipError_t go_pair_tb(int TB, const uint8_t *codes, const uint16_t *scales, int 
     case 3: return go_pair<MT, 3>(codes, scales, N, K, X, M, Y, s);
     case 4: return go_pair<MT, 4>(codes, scales, N, K, X, M, Y, s);
     case 5: return go_pair<MT, 5>(codes, scales, N, K, X, M, Y, s);
-    case 6: return go_pair<MT, 6>(codes, scales, N, K, X, M, Y, s);
+    // (MT = 2 with 6 tiles spills registers at one step in flight; 7 does not)
+    case 6: return go_pair<MT, MT == 2 ? 7 : 6>(codes, scales, N, K, X, M, Y, s);
     case 7: return go_pair<MT, 7>(codes, scales, N, K, X, M, Y, s);
     default: return go_pair<MT, 8>(codes, scales, N, K, X, M, Y, s);
   }
