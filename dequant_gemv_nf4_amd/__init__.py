@@ -26,6 +26,7 @@ from ._lib import (  # noqa: F401
     lib_path,
     nf4_codebook,
     nf4_embed,
+    nf4_gemm_prefill,
     nf4_gemm_smallm,
     nf4_gemv,
     nf4_pack,

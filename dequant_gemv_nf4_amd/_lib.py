@@ -45,6 +45,7 @@ def _load():
     L.nf4_unpack.argtypes = [vp, vp, i64, i64, vp, vp]
     L.nf4_gemv.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     L.nf4_gemm_smallm.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp]
+    L.nf4_gemm_prefill.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp]
     L.nf4_embed.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, vp]
     L.nf4_ring_create.argtypes = [ctypes.POINTER(ctypes.c_void_p), vp, vp, i64, vp, vp]
     L.nf4_ring_gemm.argtypes = [vp, vp, vp, i64, i64, vp, i64, vp]
@@ -53,7 +54,8 @@ def _load():
     L.nf4_ring_slot_bytes.restype = ctypes.c_int64
     for f in (L.nf4_ring_create, L.nf4_ring_gemm, L.nf4_ring_destroy):
         f.restype = ctypes.c_int
-    for f in (L.nf4_pack, L.nf4_unpack, L.nf4_gemv, L.nf4_gemm_smallm, L.nf4_embed):
+    for f in (L.nf4_pack, L.nf4_unpack, L.nf4_gemv, L.nf4_gemm_smallm, L.nf4_gemm_prefill,
+              L.nf4_embed):
         f.restype = ctypes.c_int
     L.nf4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
     L.nf4_codebook.restype = None
@@ -157,6 +159,23 @@ def nf4_gemm_smallm(codes, scales, X, Y, stream=None):
         _check("nf4_gemm_smallm", _load().nf4_gemm_smallm(_ptr(codes), _ptr(scales), N, K,
                                                           _ptr(X), M, _ptr(Y),
                                                           _stream(X.device, stream)))
+
+
+def nf4_gemm_prefill(codes, scales, X, Y, stream=None):
+    """Y [M][N] (fp32) = X . dequant(codes, scales)^T, X bf16 [M][K], any M >= 1
+    (M * K < 2^30), on the large-tile MFMA kernel."""
+    _need(codes, "codes", (torch.uint8,), (2,))
+    _need(scales, "scales", _U16 + (torch.float16,))
+    _need(X, "X", _BF16, (1, 2))
+    _need(Y, "Y", (torch.float32,))
+    M, K = (1, X.shape[0]) if X.dim() == 1 else X.shape
+    N = _nk(codes, scales, K)
+    if Y.numel() != M * N:
+        raise ValueError("Y must have M*N elements")
+    with torch.cuda.device(X.device):
+        _check("nf4_gemm_prefill", _load().nf4_gemm_prefill(_ptr(codes), _ptr(scales), N, K,
+                                                            _ptr(X), M, _ptr(Y),
+                                                            _stream(X.device, stream)))
 
 
 def nf4_embed(codes, scales, K, ids, out, dev_status=None, stream=None):
@@ -278,7 +297,12 @@ def embed(codes, scales, K, ids, stream=None):
 
 
 def gemm(codes, scales, X, stream=None):
+    """Y = X . dequant(codes, scales)^T for any M: up to MAX_M rows on the
+    small-batch kernels, beyond that on the prefill tiles."""
     M = 1 if X.dim() == 1 else X.shape[0]
     Y = torch.empty((M, codes.shape[0]), dtype=torch.float32, device=X.device)
-    nf4_gemm_smallm(codes, scales, X, Y, stream)
+    if M <= MAX_M:
+        nf4_gemm_smallm(codes, scales, X, Y, stream)
+    else:
+        nf4_gemm_prefill(codes, scales, X, Y, stream)
     return Y

@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnf4.so")
-SOURCES = ["api.hip", "pack.hip", "gemv.hip", "gemm_mfma.hip", "embed.hip", "ring.hip"]
+SOURCES = ["api.hip", "pack.hip", "gemv.hip", "gemm_mfma.hip", "gemm_prefill.hip", "embed.hip", "ring.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

@@ -87,6 +87,18 @@ int nf4_gemm_smallm(const uint8_t *codes, const uint16_t *scales, int64_t N, int
   return launched(nf4::launch_gemm_mfma(codes, scales, N, K, X, m, Y, s));
 }
 
+int nf4_gemm_prefill(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                     const uint16_t *X, int64_t M, float *Y, void *stream) {
+  if (!codes || !scales || !X || !Y) return NF4_EINVAL;
+  if (int r = check_shape(N, K)) return r;
+  if (M < 1 || M * K >= (int64_t(1) << 30)) return NF4_ERANGE;  // X below 2 GiB
+  if (!aligned(codes, 16) || !aligned(scales, 2) || !aligned(X, 16) || !aligned(Y, 4))
+    return NF4_EALIGN;
+  if (int r = check_device()) return r;
+  return launched(
+      nf4::launch_gemm_prefill(codes, scales, N, K, X, M, Y, (hipStream_t)stream));
+}
+
 int nf4_gemv(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
              const uint16_t *x, float *y, void *stream) {
   return nf4_gemm_smallm(codes, scales, N, K, x, 1, y, stream);

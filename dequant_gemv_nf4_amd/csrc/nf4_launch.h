@@ -19,6 +19,11 @@ hipError_t launch_gemv_valu(const uint8_t *codes, const uint16_t *scales, int64_
 hipError_t launch_gemm_mfma(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
                             const uint16_t *X, int M, float *Y, hipStream_t stream);
 
+// MFMA product with 64 x 64 .. 128 x 128 workgroup tiles, any M >= 1 (prefill).
+hipError_t launch_gemm_prefill(const uint8_t *codes, const uint16_t *scales, int64_t N,
+                               int64_t K, const uint16_t *X, int64_t M, float *Y,
+                               hipStream_t stream);
+
 // Packed embedding rows into bf16; status (may be null) is cleared first.
 hipError_t launch_embed(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
                         const int64_t *ids, int64_t T, uint16_t *out, int32_t *status,

@@ -32,6 +32,7 @@ def lib():
     L.nf4_unpack.argtypes = [vp, vp, i64, i64, vp, vp]
     L.nf4_gemv.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     L.nf4_gemm_smallm.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp]
+    L.nf4_gemm_prefill.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp]
     L.nf4_embed.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, vp]
     L.nf4_ring_create.argtypes = [ctypes.POINTER(ctypes.c_void_p), vp, vp, i64, vp, vp]
     L.nf4_ring_gemm.argtypes = [vp, vp, vp, i64, i64, vp, i64, vp]
@@ -44,7 +45,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = _declared()
-    for required in ("nf4_pack", "nf4_unpack", "nf4_gemv", "nf4_gemm_smallm", "nf4_embed",
+    for required in ("nf4_pack", "nf4_unpack", "nf4_gemv", "nf4_gemm_smallm", "nf4_gemm_prefill",
+                     "nf4_embed",
                      "nf4_ring_create", "nf4_ring_gemm", "nf4_ring_slot_bytes", "nf4_ring_destroy",
                      "nf4_codebook", "nf4_strerror"):
         assert required in names
@@ -76,6 +78,7 @@ EINVAL, EALIGN, ERANGE = -1, -2, -3
 def test_shape_validation(lib, N, K, expect):
     assert lib.nf4_gemv(P, P, N, K, P, P, NULL) == expect
     assert lib.nf4_gemm_smallm(P, P, N, K, P, 4, P, NULL) == expect
+    assert lib.nf4_gemm_prefill(P, P, N, K, P, 64, P, NULL) == expect
     assert lib.nf4_pack(P, N, K, P, P, NULL, NULL) == expect
     assert lib.nf4_unpack(P, P, N, K, P, NULL) == expect
     assert lib.nf4_embed(P, P, N, K, P, 4, P, NULL, NULL) == expect
@@ -93,6 +96,21 @@ def test_null_pointers(lib):
 @pytest.mark.parametrize("M", [0, -3, 33, 1000])
 def test_m_range(lib, M):
     assert lib.nf4_gemm_smallm(P, P, 4, 64, P, M, P, NULL) == ERANGE
+
+
+@pytest.mark.parametrize("M,K", [(0, 64), (-3, 64), (2 ** 24, 64), (2 ** 15, 32768)])
+def test_prefill_m_range(lib, M, K):
+    assert lib.nf4_gemm_prefill(P, P, 4, K, P, M, P, NULL) == ERANGE
+
+
+def test_prefill_null_and_alignment(lib):
+    for args in ((NULL, P, P, P), (P, NULL, P, P), (P, P, NULL, P), (P, P, P, NULL)):
+        c, s, x, y = args
+        assert lib.nf4_gemm_prefill(c, s, 4, 64, x, 64, y, NULL) == EINVAL
+    assert lib.nf4_gemm_prefill(P_ODD, P, 4, 64, P, 64, P, NULL) == EALIGN
+    assert lib.nf4_gemm_prefill(P, ctypes.c_void_p(0x100001), 4, 64, P, 64, P, NULL) == EALIGN
+    assert lib.nf4_gemm_prefill(P, P, 4, 64, P_ODD, 64, P, NULL) == EALIGN
+    assert lib.nf4_gemm_prefill(P, P, 4, 64, P, 64, P_ODD, NULL) == EALIGN
 
 
 def test_alignment(lib):
