@@ -27,8 +27,9 @@
 //   - the group's 32 x 32 tile (fp32) is multiplied by s(n, g) * 2^-shift(m, g)
 //     and added to the fp32 accumulator.  No weight is rounded together with
 //     its scale.
-// Loads for step g+1 (activations, codes, scales) are issued before step g
-// computes; the activation stage is double-buffered in LDS, one barrier a step.
+// A register ring keeps the loads of the next four (two, for 128 x 128) groups (activations, codes,
+// scales) in flight; the activation stage is double-buffered in LDS, one
+// barrier a step.
 // Rows past M and columns past N re-read the last valid row or column and are
 // never stored.  No atomics, no cross-workgroup traffic: bitwise reproducible.
 #include <utility>
@@ -61,7 +62,12 @@ __device__ __forceinline__ uint32_t max8(uint32_t v) {
   return v;
 }
 
-template <int RM, int CN>
+template <typename F, int... d>
+__device__ __forceinline__ void for_slots(F &&f, std::integer_sequence<int, d...>) {
+  (f(std::integral_constant<int, d>{}), ...);
+}
+
+template <int RM, int CN, int P>
 __global__ void __launch_bounds__(kPThreads)
     gemm_prefill_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
                         const uint16_t *__restrict__ X, float *__restrict__ Y, int N, int K,
@@ -104,14 +110,16 @@ __global__ void __launch_bounds__(kPThreads)
     svo[c] = n * NG * 2;
   }
 
-  u32x4_t xr[kXChunks];
-  u32x4_t cr[2][CN];
-  uint32_t sr[2][CN];
-  auto load_x = [&](int g) __attribute__((always_inline)) {
+  // a ring of P groups in flight: slot d holds the loads of groups g = d (mod P)
+  u32x4_t xr[P][kXChunks];
+  u32x4_t cr[P][CN];
+  uint32_t sr[P][CN];
+  auto load_x = [&](auto slot, int g) __attribute__((always_inline)) {
+    constexpr int d = decltype(slot)::value;
     const int gs = __builtin_amdgcn_readfirstlane(min(g, NG - 1));
 #pragma unroll
     for (int j = 0; j < kXChunks; ++j)
-      xr[j] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xvo[j], 128 * gs, 0);
+      xr[d][j] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xvo[j], 128 * gs, 0);
   };
   auto load_w = [&](auto slot, int g) __attribute__((always_inline)) {
     constexpr int d = decltype(slot)::value;
@@ -132,14 +140,15 @@ __global__ void __launch_bounds__(kPThreads)
       for (int i = 0; i < 16; ++i) acc[r][c][i] = 0.f;
 
   const uint32_t laneoff = 4u * lane;
-  // one step: stage group g's activations, prefetch group g + 1, multiply
+  // one step: stage group g's activations, refill the slot's activations with
+  // group g + P, multiply, refill the slot's codes and scales
   auto step = [&](auto slot, int g) __attribute__((always_inline)) {
     constexpr int d = decltype(slot)::value;
-    uint8_t *const xb = xs + d * kStage;
-    float *const fb = fm + d * BM;
+    uint8_t *const xb = xs + (d & 1) * kStage;
+    float *const fb = fm + (d & 1) * BM;
 #pragma unroll
     for (int j = 0; j < kXChunks; ++j) {
-      const u32x4_t v = xr[j];
+      const u32x4_t v = xr[d][j];
       uint32_t mx = max(max(bf16x2_absmax_bits(v[0]), bf16x2_absmax_bits(v[1])),
                         max(bf16x2_absmax_bits(v[2]), bf16x2_absmax_bits(v[3])));
       mx = max8(mx);
@@ -151,8 +160,7 @@ __global__ void __launch_bounds__(kPThreads)
       if (part == 0) fb[row] = ldexpf(1.0f, -sh);
     }
     __syncthreads();
-    load_x(g + 1);
-    load_w(std::integral_constant<int, d ^ 1>{}, g + 1);
+    load_x(slot, g + P);
 
     f32x16_t t[RM][CN];
 #pragma unroll
@@ -204,18 +212,29 @@ __global__ void __launch_bounds__(kPThreads)
         for (int i = 0; i < 16; ++i) acc[r][c][i] = fmaf(t[r][c][i], f[i] * sc, acc[r][c][i]);
       }
     }
+    load_w(slot, g + P);
+    __builtin_amdgcn_sched_barrier(0);  // refills stay after the step that frees the slot
   };
 
-  load_x(0);
-  load_w(std::integral_constant<int, 0>{}, 0);
+  // (issued in the loop's order: activations, then codes and scales, per group)
+  for_slots(
+      [&](auto slot) __attribute__((always_inline)) {
+        load_x(slot, decltype(slot)::value);
+        load_w(slot, decltype(slot)::value);
+        __builtin_amdgcn_sched_barrier(0);
+      },
+      std::make_integer_sequence<int, P>{});
   build_byte_lut(lut, tid, kPThreads);
 
   int g = 0;
-  for (; g + 2 <= NG; g += 2) {
-    step(std::integral_constant<int, 0>{}, g);
-    step(std::integral_constant<int, 1>{}, g + 1);
-  }
-  if (g < NG) step(std::integral_constant<int, 0>{}, g);
+  for (; g + P <= NG; g += P)
+    for_slots([&](auto slot) __attribute__((always_inline)) { step(slot, g + decltype(slot)::value); },
+              std::make_integer_sequence<int, P>{});
+  for_slots(
+      [&](auto slot) __attribute__((always_inline)) {
+        if (g + decltype(slot)::value < NG) step(slot, g + decltype(slot)::value);
+      },
+      std::make_integer_sequence<int, P>{});
 
 #pragma unroll
   for (int r = 0; r < RM; ++r)
@@ -238,7 +257,10 @@ template <int RM, int CN>
 hipError_t go_prefill(const uint8_t *codes, const uint16_t *scales, int N, int K,
                       const uint16_t *X, int M, float *Y, hipStream_t stream) {
   const dim3 grid(cdiv(N, 64 * CN), cdiv(M, 64 * RM));
-  hipLaunchKernelGGL((gemm_prefill_kernel<RM, CN>), grid, dim3(kPThreads), 0, stream, codes,
+  // groups in flight (even: the LDS stage alternates); the 128 x 128 tile has
+  // room in registers for two only
+  constexpr int P = RM * CN == 4 ? 2 : 4;
+  hipLaunchKernelGGL((gemm_prefill_kernel<RM, CN, P>), grid, dim3(kPThreads), 0, stream, codes,
                      scales, X, Y, N, K, M);
   return hipGetLastError();
 }
