@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16 / bf16 matrix cores, published
 METRIC = "NF4 GEMV effective HBM GB/s and % of peak at M=1; µs/layer-set (7B shapes)"
 
 
@@ -42,6 +43,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--set", default="llama2-7b",
                     help="layer set: llama2-7b, llama2-13b, llama2-70b, llama3.1-8b-smallm, "
+                         "llama3.1-8b-prefill (use with --m 64..512), "
                          "single-4096x4096")
     ap.add_argument("--m", type=int, default=1, help="activation rows per product")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = set's)")
@@ -277,7 +279,9 @@ def bench_copyring(args, torch, dev):
     out = {"metric": RING_METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
            "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "nf4-w/bf16-x/f16-dot/fp32-acc", "data": "synthetic",
+           "dtype": ("nf4-w/bf16-x/f16-dot/fp32-acc" if M < 8 else
+                  "nf4-w/bf16-x/bf16-mfma/fp32-acc" if M <= nf4.MAX_M else
+                  "nf4-w/bf16-x/f16-mfma/fp32-acc"), "data": "synthetic",
            "config": {"workload": f"{set_.name} layer set through CopyRing, M={M}", "layers": L,
                       "packed_gb": round(packed / 1e9, 3), "slot_mb": round(slot / 1e6, 2),
                       "timing": "eager (two streams)"},
@@ -363,8 +367,10 @@ def main():
         _, N, K, codes, scales, X, Y = it
         if M == 1:
             nf4.nf4_gemv(codes, scales, X, Y)
-        else:
+        elif M <= nf4.MAX_M:
             nf4.nf4_gemm_smallm(codes, scales, X, Y)
+        else:
+            nf4.nf4_gemm_prefill(codes, scales, X, Y)
 
     def sweep():
         for it in items:
@@ -468,6 +474,24 @@ def main():
     achieved = float(np.mean(dom["launch_bytes"]) / np.mean(dom["launch_us"]) / 1e3)
     kernel_sum_us = sum(per_proj[p]["us_mean"] * sum(1 for it in items if it[0] == p)
                         for p in order)
+    # the dominant kernel's roofline: the HBM stream, or the matrix cores once the
+    # flops per launch take longer at their peak than the bytes at theirs
+    flops = float(np.mean([2.0 * M * per_proj[p]["N"] * per_proj[p]["K"] for p in dom["projs"]]))
+    us_launch = float(np.mean(dom["launch_us"]))
+    if flops / (MFMA_F16_PEAK_TFLOPS * 1e6) > np.mean(dom["launch_bytes"]) / (HBM_PEAK_GBS * 1e3):
+        tf = flops / us_launch / 1e6
+        roof = {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                "flops_per_launch": flops}
+    else:
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    kname = ("gemv_valu_kernel" if M < 8 else "gemm_mfma_kernel" if M <= nf4.MAX_M
+             else "gemm_prefill_kernel")
+    roof.update({"traffic": recorded_traffic(f"M={M} {set_.name} " + ",".join(dom["projs"])),
+                 "kernel": f"{kname} (M={M}, K={dom_k})", "projections": dom["projs"],
+                 "bytes_per_launch": float(np.mean(dom["launch_bytes"])),
+                 "us_per_launch": round(us_launch, 3)})
 
     out = {
         "metric": METRIC,
@@ -480,7 +504,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nf4-w/bf16-x/f16-dot/fp32-acc",
+        "dtype": ("nf4-w/bf16-x/f16-dot/fp32-acc" if M < 8 else
+                  "nf4-w/bf16-x/bf16-mfma/fp32-acc" if M <= nf4.MAX_M else
+                  "nf4-w/bf16-x/f16-mfma/fp32-acc"),
         "data": "synthetic",
         "config": {"workload": f"{set_.name} layer set, M={M}", "layers": L,
                    "projections": [[p, N, K] for p, N, K in set_.projections],
@@ -494,14 +520,7 @@ def main():
         "us_per_layer_set": round(ms_per_step * 1e3 / L, 3),
         "kernel_us_per_layer_set": round(kernel_sum_us / L, 3),
         "per_projection": per_proj,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(f"M={M} {set_.name} " + ",".join(dom["projs"])),
-                     "kernel": f"gemv_valu_kernel (M={M}, K={dom_k})" if M < 8 else
-                               f"gemm_mfma_kernel (M={M}, K={dom_k})",
-                     "projections": dom["projs"],
-                     "bytes_per_launch": float(np.mean(dom["launch_bytes"])),
-                     "us_per_launch": round(float(np.mean(dom["launch_us"])), 3)},
+        "roofline": roof,
     }
     if not args.no_cpu_baseline:
         log("cpu baseline ...")

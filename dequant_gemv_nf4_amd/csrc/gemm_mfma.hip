@@ -38,6 +38,7 @@
 
 #include "nf4_device.h"
 #include "nf4_launch.h"
+#include "nf4_split.h"
 
 namespace nf4 {
 
@@ -48,28 +49,6 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 512;  // 8 waves
 constexpr int kWaves = kThreads / 64;
-
-// ---------------------------------------------------------------------------
-// bf16 hi / lo split of the levels, at compile time (round to nearest even).
-// ---------------------------------------------------------------------------
-constexpr uint32_t bf16_rne_bits(uint32_t f) { return (f + 0x7fffu + ((f >> 16) & 1u)) >> 16; }
-
-struct LevelSplit {
-  uint32_t hi[16];
-  uint32_t lo[16];
-};
-constexpr LevelSplit make_level_split() {
-  LevelSplit r{};
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t h = bf16_rne_bits(kLevelBits[i]);
-    const float rest =
-        __builtin_bit_cast(float, kLevelBits[i]) - __builtin_bit_cast(float, h << 16);
-    r.hi[i] = h;
-    r.lo[i] = bf16_rne_bits(__builtin_bit_cast(uint32_t, rest));
-  }
-  return r;
-}
-constexpr LevelSplit kSplit = make_level_split();
 
 // Entry b (b = 16 h + j, j = low nibble = even k) at byte 256 b + 8 c, copy c:
 //   word 0 = hi[j] | hi[h] << 16,  word 1 = lo[j] | lo[h] << 16.

@@ -35,13 +35,13 @@
  * memory is touched.  Asynchronous GPU faults surface on the stream as usual.
  *
  * Numerics: nf4_pack and nf4_unpack are exact (bit-for-bit defined below).
- * nf4_gemv / nf4_gemm_smallm accumulate in fp32.  Below M = 8 the levels are
- * f16 and each activation block is scaled by a power of two into f16; from
- * M = 8 the levels are split into bf16 hi + lo and the bf16 activations are used
- * as they are.  nf4_gemm_prefill uses f16 levels and scales each activation
- * row's 64 values of a group by a power of two into f16.  Per output element |Y - Y_exact| <= 2e-3 * sum_k |w~(n,k) X[m][k]|
- * + 1e-5 for finite inputs whose products stay in range.  Results are
- * deterministic: the same call on the same device gives the same bits.
+ * The products accumulate in fp32.  Below M = 8 the levels are f16 and each
+ * activation block is scaled by a power of two into f16; from M = 8 (and in
+ * nf4_gemm_prefill) the levels are split into bf16 hi + lo and the bf16
+ * activations are used as they are.  Per output element
+ * |Y - Y_exact| <= 2e-3 * sum_k |w~(n,k) X[m][k]| + 1e-5 for finite inputs whose
+ * products stay in range.  Results are deterministic: the same call on the same
+ * device gives the same bits.
  */
 #ifndef NF4_H
 #define NF4_H
@@ -118,7 +118,7 @@ int nf4_gemm_smallm(const uint8_t *codes, const uint16_t *scales, int64_t N, int
 /*
  * nf4_gemm_prefill -- the same product, Y[m][n] = sum_k L[code(n,k)] *
  * s(n,k/64) * X[m][k], for any batch 1 <= M with M * K < 2^30 (prefill chunks
- * beyond 32 positions), on 32 x 32 x 16 f16 MFMA tiles of 64 x 64 to 128 x 128
+ * beyond 32 positions), on 32 x 32 x 16 bf16 MFMA tiles of 64 x 64 to 128 x 128
  * outputs per workgroup.  Source: deep-fold README, "Method" (prefill on the
  * NF4 matrix-core product); Trapetum home page, "The fine print" (at prefill
  * sizes the product is bound by arithmetic, not by the weight stream).

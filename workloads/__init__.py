@@ -41,8 +41,10 @@ SET_7B = LayerSet("llama2-7b", tuple(LLAMA2_7B), 32, 0.02)
 SET_13B = LayerSet("llama2-13b", tuple(LLAMA2_13B), 40, 0.02)
 SET_70B = LayerSet("llama2-70b", tuple(LLAMA2_70B), 80, 0.015)
 SET_8B_SMALLM = LayerSet("llama3.1-8b-smallm", tuple(LLAMA31_8B), 32, 0.02, (4, 8, 32))
+SET_8B_PREFILL = LayerSet("llama3.1-8b-prefill", tuple(LLAMA31_8B), 32, 0.02, (64, 128, 256, 512))
 
-ALL_SETS = {s.name: s for s in (SINGLE_4096, SET_7B, SET_13B, SET_70B, SET_8B_SMALLM)}
+ALL_SETS = {s.name: s for s in (SINGLE_4096, SET_7B, SET_13B, SET_70B, SET_8B_SMALLM,
+                                SET_8B_PREFILL)}
 
 
 # Projections of one decoder layer that read the same activation vector: q, k and v
