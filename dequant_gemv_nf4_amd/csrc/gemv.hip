@@ -198,24 +198,28 @@ __global__ void __launch_bounds__(kThreads)
   float xf[M][UPL];  // 2^-shift of each unit
   uint4 *stage_x = reinterpret_cast<uint4 *>(stage);                 // [4][M][U]
   int *stage_sh = reinterpret_cast<int *>(stage + M * U * 64);       // [M][U]
+  // (only the chunks a wave loaded: the loop is unrolled for the largest M K,
+  // and work on unloaded chunks would cost the whole wave its set-up time)
 #pragma unroll
   for (int j = 0; j < kXChunks; ++j) {
-    const int c = tid + j * kThreads;
-    const uint4 v = xr[j];
-    uint32_t mx = max(max(bf16x2_absmax_bits(v.x), bf16x2_absmax_bits(v.y)),
-                      max(bf16x2_absmax_bits(v.z), bf16x2_absmax_bits(v.w)));
-    mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0xB1, 0xf, 0xf, false));
-    mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x4E, 0xf, 0xf, false));
-    if (c < nchunks) {  // nchunks is a multiple of 4: a quad is valid or not as a whole
-      const int sh = f16_range_shift(mx);
-      const int q = c & 3;
-      const int mu = c >> 2;  // m * U + u
-      const int m = mu / U;
-      const int u = mu - m * U;
-      stage_x[(q * M + m) * U + u] =
-          make_uint4(bf16x2_to_f16x2(v.x, sh), bf16x2_to_f16x2(v.y, sh),
-                     bf16x2_to_f16x2(v.z, sh), bf16x2_to_f16x2(v.w, sh));
-      if (q == 0) stage_sh[mu] = sh;
+    if (wave_chunk0 + j * kThreads < nchunks) {  // uniform per wave
+      const int c = tid + j * kThreads;
+      const uint4 v = xr[j];
+      uint32_t mx = max(max(bf16x2_absmax_bits(v.x), bf16x2_absmax_bits(v.y)),
+                        max(bf16x2_absmax_bits(v.z), bf16x2_absmax_bits(v.w)));
+      mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0xB1, 0xf, 0xf, false));
+      mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x4E, 0xf, 0xf, false));
+      if (c < nchunks) {  // nchunks is a multiple of 4: a quad is valid or not as a whole
+        const int sh = f16_range_shift(mx);
+        const int q = c & 3;
+        const int mu = c >> 2;  // m * U + u
+        const int m = mu / U;
+        const int u = mu - m * U;
+        stage_x[(q * M + m) * U + u] =
+            make_uint4(bf16x2_to_f16x2(v.x, sh), bf16x2_to_f16x2(v.y, sh),
+                       bf16x2_to_f16x2(v.z, sh), bf16x2_to_f16x2(v.w, sh));
+        if (q == 0) stage_sh[mu] = sh;
+      }
     }
   }
   __syncthreads();
