@@ -1,0 +1,92 @@
+"""Host logic of the bench and the workload definitions (no GPU needed): the
+one-GPU contract of bench.py, the recorded HBM-traffic lookup, the same-x launch
+groups, the algorithmic byte count, seed separation and the CPU-baseline leg."""
+import hashlib
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402  (module import runs nothing)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_recorded_traffic_follows_the_source_hash():
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    table = json.load(open(path))
+    for key, entry in table.items():
+        if key.startswith("_"):
+            continue
+        src = b"".join(open(os.path.join(ROOT, f), "rb").read() for f in entry["sources"])
+        fresh = hashlib.sha256(src).hexdigest() == entry["source_sha256"]
+        got = bench.recorded_traffic(key)
+        assert got == (entry["bytes_per_launch"] if fresh else None), key
+        assert entry["bytes_per_launch"] == entry["read_bytes_per_launch"] + \
+            entry["write_bytes_per_launch"]
+    assert bench.recorded_traffic("no such kernel") is None
+
+
+def test_launch_groups_fuse_same_x_projections():
+    fused = wl.launch_groups(wl.SET_7B, fused=True)
+    assert [(n, sum(N for _, N, _ in p), p[0][2]) for n, p in fused] == [
+        ("q|k|v", 12288, 4096), ("o", 4096, 4096), ("gate|up", 22016, 4096),
+        ("down", 4096, 11008)]
+    plain = wl.launch_groups(wl.SET_7B, fused=False)
+    assert [n for n, _ in plain] == ["q", "k", "v", "o", "gate", "up", "down"]
+    # GQA: k and v are narrower but read the same x, so they still fuse
+    fused70 = wl.launch_groups(wl.SET_70B, fused=True)
+    assert fused70[0][0] == "q|k|v" and sum(N for _, N, _ in fused70[0][1]) == 10240
+    # every projection appears exactly once either way
+    for s in wl.ALL_SETS.values():
+        for f in (True, False):
+            got = [p for _, grp in wl.launch_groups(s, f) for p in grp]
+            assert got == list(s.projections), (s.name, f)
+
+
+@pytest.mark.parametrize("N,K,M", [(4096, 4096, 1), (11008, 4096, 1), (1024, 8192, 32),
+                                   (64, 64, 512)])
+def test_algorithmic_bytes(N, K, M):
+    # codes 4 bits, one fp16 per 64 weights, bf16 activations, fp32 outputs
+    assert wl.algorithmic_bytes(N, K, M) == N * K * 17 // 32 + 2 * M * K + 4 * M * N
+
+
+def test_seeds_are_distinct():
+    seen = set()
+    for s in wl.ALL_SETS.values():
+        for layer in range(4):
+            for proj, _, _ in s.projections:
+                for kind in ("W", "x"):
+                    seen.add(wl.seed_for(s.name, layer, proj, kind))
+    n = sum(len(s.projections) for s in wl.ALL_SETS.values()) * 4 * 2
+    assert len(seen) == n
+
+
+def test_generators_are_seeded_and_shaped():
+    a = wl.weights(3, 128, 0.02, seed=7)
+    b = wl.weights(3, 128, 0.02, seed=7)
+    c = wl.weights(3, 128, 0.02, seed=8)
+    assert a.shape == (3, 128) and bool((a == b).all()) and not bool((a == c).all())
+    x = wl.activations(2, 64, seed=9)
+    assert str(x.dtype) == "torch.bfloat16" and tuple(x.shape) == (2, 64)
+    assert 0.01 < float(a.std()) < 0.03
+
+
+def test_cpu_baseline_leg_reports_the_contract_keys():
+    out = bench.cpu_baseline(wl.SINGLE_4096, 1, 0.05)
+    assert set(out) >= {"value", "unit", "cores", "kind", "sample"}
+    assert out["kind"] == "oracle" and out["cores"] == 1 and out["value"] > 0
+    assert np.isfinite(out["value"])
