@@ -363,12 +363,19 @@ def main():
     log(f"packed {packed_bytes / 1e9:.2f} GB in {time.perf_counter() - t0:.1f} s; "
         f"{step_bytes / 1e6:.2f} MB algorithmic per step")
 
+    # one workspace for the small-batch products that split K over workgroups:
+    # every launch runs on one stream after the previous, and each call leaves
+    # the workspace's counters re-armed
+    ws_bytes = max([nf4.smallm_workspace_bytes(N, K, M) for _, N, K, *_ in items]
+                   if 1 < M <= nf4.MAX_M else [0])
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+
     def launch(it):
         _, N, K, codes, scales, X, Y = it
         if M == 1:
             nf4.nf4_gemv(codes, scales, X, Y)
         elif M <= nf4.MAX_M:
-            nf4.nf4_gemm_smallm(codes, scales, X, Y)
+            nf4.nf4_gemm_smallm_ws(codes, scales, X, Y, ws)
         else:
             nf4.nf4_gemm_prefill(codes, scales, X, Y)
 

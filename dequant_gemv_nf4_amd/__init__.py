@@ -28,10 +28,13 @@ from ._lib import (  # noqa: F401
     nf4_embed,
     nf4_gemm_prefill,
     nf4_gemm_smallm,
+    nf4_gemm_smallm_ws,
     nf4_gemv,
     nf4_pack,
     nf4_unpack,
     pack,
     ring_slot_bytes,
+    smallm_workspace_bytes,
     unpack,
+    workspace_for,
 )

@@ -46,6 +46,9 @@ def _load():
     L.nf4_gemv.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     L.nf4_gemm_smallm.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp]
     L.nf4_gemm_prefill.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp]
+    L.nf4_gemm_smallm_ws.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, i64, vp]
+    L.nf4_gemm_smallm_workspace_bytes.argtypes = [i64, i64, i64]
+    L.nf4_gemm_smallm_workspace_bytes.restype = ctypes.c_int64
     L.nf4_embed.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, vp]
     L.nf4_ring_create.argtypes = [ctypes.POINTER(ctypes.c_void_p), vp, vp, i64, vp, vp]
     L.nf4_ring_gemm.argtypes = [vp, vp, vp, i64, i64, vp, i64, vp]
@@ -54,8 +57,8 @@ def _load():
     L.nf4_ring_slot_bytes.restype = ctypes.c_int64
     for f in (L.nf4_ring_create, L.nf4_ring_gemm, L.nf4_ring_destroy):
         f.restype = ctypes.c_int
-    for f in (L.nf4_pack, L.nf4_unpack, L.nf4_gemv, L.nf4_gemm_smallm, L.nf4_gemm_prefill,
-              L.nf4_embed):
+    for f in (L.nf4_pack, L.nf4_unpack, L.nf4_gemv, L.nf4_gemm_smallm, L.nf4_gemm_smallm_ws,
+              L.nf4_gemm_prefill, L.nf4_embed):
         f.restype = ctypes.c_int
     L.nf4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
     L.nf4_codebook.restype = None
@@ -159,6 +162,52 @@ def nf4_gemm_smallm(codes, scales, X, Y, stream=None):
         _check("nf4_gemm_smallm", _load().nf4_gemm_smallm(_ptr(codes), _ptr(scales), N, K,
                                                           _ptr(X), M, _ptr(Y),
                                                           _stream(X.device, stream)))
+
+
+def smallm_workspace_bytes(N, K, M):
+    """Bytes of workspace nf4_gemm_smallm_ws needs for (N, K, M); 0 = no split."""
+    n = _load().nf4_gemm_smallm_workspace_bytes(int(N), int(K), int(M))
+    if n < 0:
+        raise ValueError(f"invalid shape N={N} K={K} M={M}")
+    return int(n)
+
+
+def nf4_gemm_smallm_ws(codes, scales, X, Y, workspace, stream=None):
+    """nf4_gemm_smallm with a device workspace (uint8 tensor, counters zeroed
+    before its first use; or None when smallm_workspace_bytes is 0)."""
+    _need(codes, "codes", (torch.uint8,), (2,))
+    _need(scales, "scales", _U16 + (torch.float16,))
+    _need(X, "X", _BF16, (1, 2))
+    _need(Y, "Y", (torch.float32,))
+    M, K = (1, X.shape[0]) if X.dim() == 1 else X.shape
+    N = _nk(codes, scales, K)
+    if Y.numel() != M * N:
+        raise ValueError("Y must have M*N elements")
+    nbytes = 0
+    if workspace is not None:
+        _need(workspace, "workspace", (torch.uint8,))
+        nbytes = workspace.numel()
+    with torch.cuda.device(X.device):
+        _check("nf4_gemm_smallm_ws", _load().nf4_gemm_smallm_ws(
+            _ptr(codes), _ptr(scales), N, K, _ptr(X), M, _ptr(Y), _ptr(workspace), nbytes,
+            _stream(X.device, stream)))
+
+
+# one workspace per (device, stream): calls sharing one must not overlap, and
+# calls on one stream never do
+_workspaces = {}
+
+
+def workspace_for(device, nbytes, stream=None):
+    """A zero-initialised workspace of at least nbytes for calls on `stream`
+    (default: the current stream) of `device`, kept and reused."""
+    device = torch.device(device)
+    key = (device.index, _stream(device, stream).value)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
 
 
 def nf4_gemm_prefill(codes, scales, X, Y, stream=None):
@@ -298,11 +347,16 @@ def embed(codes, scales, K, ids, stream=None):
 
 def gemm(codes, scales, X, stream=None):
     """Y = X . dequant(codes, scales)^T for any M: up to MAX_M rows on the
-    small-batch kernels, beyond that on the prefill tiles."""
+    small-batch kernels (with a kept workspace where K splits over workgroups),
+    beyond that on the prefill tiles."""
     M = 1 if X.dim() == 1 else X.shape[0]
     Y = torch.empty((M, codes.shape[0]), dtype=torch.float32, device=X.device)
     if M <= MAX_M:
-        nf4_gemm_smallm(codes, scales, X, Y, stream)
+        need = smallm_workspace_bytes(codes.shape[0], X.shape[-1], M)
+        if need:
+            nf4_gemm_smallm_ws(codes, scales, X, Y, workspace_for(X.device, need, stream), stream)
+        else:
+            nf4_gemm_smallm(codes, scales, X, Y, stream)
     else:
         nf4_gemm_prefill(codes, scales, X, Y, stream)
     return Y

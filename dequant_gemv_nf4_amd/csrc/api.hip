@@ -69,6 +69,35 @@ int nf4_unpack(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t 
   return launched(nf4::launch_unpack(codes, scales, N, K, W_out, (hipStream_t)stream));
 }
 
+int64_t nf4_gemm_smallm_workspace_bytes(int64_t N, int64_t K, int64_t M) {
+  if (check_shape(N, K) || M < 1 || M > NF4_MAX_M) return -1;
+  if (M < 8 && nf4::valu_supported(N, K, (int)M)) return 0;
+  return nf4::gemm_mfma_workspace_bytes(N, K, (int)M);
+}
+
+int nf4_gemm_smallm_ws(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                       const uint16_t *X, int64_t M, float *Y, void *workspace,
+                       int64_t workspace_bytes, void *stream) {
+  if (!codes || !scales || !X || !Y) return NF4_EINVAL;
+  if (int r = check_shape(N, K)) return r;
+  if (M < 1 || M > NF4_MAX_M) return NF4_ERANGE;
+  if (!aligned(codes, 16) || !aligned(scales, 2) || !aligned(X, 16) || !aligned(Y, 4) ||
+      (workspace && !aligned(workspace, 256)))
+    return NF4_EALIGN;
+  const int64_t need = nf4_gemm_smallm_workspace_bytes(N, K, M);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return NF4_ERANGE;
+  if (int r = check_device()) return r;
+  const int m = (int)M;
+  hipStream_t s = (hipStream_t)stream;
+  // M < 8 on the vector ALUs (decode shared across the M dot products); the
+  // batch tiles from 8 rows up, and the rare small-M shapes whose activations do
+  // not fit the VALU kernel's registers, on MFMA.
+  if (m < 8 && nf4::valu_supported(N, K, m))
+    return launched(nf4::launch_gemv_valu(codes, scales, N, K, X, m, Y, s));
+  return launched(nf4::launch_gemm_mfma(codes, scales, N, K, X, m, Y,
+                                        need > 0 ? workspace : nullptr, workspace_bytes, s));
+}
+
 int nf4_gemm_smallm(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
                     const uint16_t *X, int64_t M, float *Y, void *stream) {
   if (!codes || !scales || !X || !Y) return NF4_EINVAL;
@@ -79,12 +108,9 @@ int nf4_gemm_smallm(const uint8_t *codes, const uint16_t *scales, int64_t N, int
   if (int r = check_device()) return r;
   const int m = (int)M;
   hipStream_t s = (hipStream_t)stream;
-  // M < 8 on the vector ALUs (decode shared across the M dot products); the
-  // batch tiles from 8 rows up, and the rare small-M shapes whose activations do
-  // not fit the VALU kernel's registers, on MFMA.
   if (m < 8 && nf4::valu_supported(N, K, m))
     return launched(nf4::launch_gemv_valu(codes, scales, N, K, X, m, Y, s));
-  return launched(nf4::launch_gemm_mfma(codes, scales, N, K, X, m, Y, s));
+  return launched(nf4::launch_gemm_mfma(codes, scales, N, K, X, m, Y, nullptr, 0, s));
 }
 
 int nf4_gemm_prefill(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,

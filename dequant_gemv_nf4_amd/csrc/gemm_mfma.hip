@@ -256,7 +256,7 @@ template <int MT, int TB, int D>
 __global__ void __launch_bounds__(kThreads)
     gemm_mfma_pair_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
                           const uint16_t *__restrict__ X, float *__restrict__ Y, int N, int K,
-                          int M) {
+                          int M, int S, uint32_t *__restrict__ cnt, float *__restrict__ part) {
   constexpr int kRedWords = kWaves * TB * MT * 4 * 64;
   constexpr int kLdsWords = kRedWords > kLutWords ? kRedWords : kLutWords;
   __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsWords];
@@ -269,7 +269,11 @@ __global__ void __launch_bounds__(kThreads)
   const int NP = NG >> 1;  // pairs per row
   const int NT = (N + 15) >> 4;
   const int t0 = blockIdx.x * TB;
-  const int nsteps = wave < NP ? (NP - 1 - wave) / kWaves + 1 : 0;
+  // K-split blockIdx.y of S takes the pair steps [p0, p0 + np)
+  const int split = blockIdx.y;
+  const int p0 = (int)((int64_t)split * NP / S);
+  const int np = (int)((int64_t)(split + 1) * NP / S) - p0;
+  const int nsteps = wave < np ? (np - 1 - wave) / kWaves + 1 : 0;
 
   const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t *>(codes), 0, (int)((int64_t)N * (K >> 1)), kBufferWord3);
@@ -300,7 +304,7 @@ __global__ void __launch_bounds__(kThreads)
 
   auto load = [&](auto slot, int i) __attribute__((always_inline)) {
     constexpr int d = decltype(slot)::value;
-    const int p = __builtin_amdgcn_readfirstlane(min(wave + kWaves * i, NP - 1));
+    const int p = __builtin_amdgcn_readfirstlane(p0 + min(wave + kWaves * i, np - 1));
 #pragma unroll
     for (int j = 0; j < TB; ++j) {
       rc[d][j] = __builtin_amdgcn_raw_buffer_load_b128(crs, cvo[j], 64 * p, kLoadStream);
@@ -404,15 +408,48 @@ __global__ void __launch_bounds__(kThreads)
         red[(((wave * TB + j) * MT + mt) * 4 + r) * 64 + lane] = acc[j][mt][r];
   __syncthreads();
   constexpr int kOut = TB * MT * 256;
-  for (int o = tid; o < kOut; o += kThreads) {
-    float sum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) sum += red[w * kOut + o];
+  auto store = [&](int o, float v) __attribute__((always_inline)) {
     const int ln = o & 63, r = (o >> 6) & 3, tm = o >> 8;
     const int mt = tm % MT, j = tm / MT;
     const int m = 16 * mt + 4 * (ln >> 4) + r;
     const int n = 16 * (t0 + j) + (ln & 15);
-    if (t0 + j < NT && m < M && n < N) Y[(int64_t)m * N + n] = sum;
+    if (t0 + j < NT && m < M && n < N) Y[(int64_t)m * N + n] = v;
+  };
+  float *const mine = S > 1 ? part + ((int64_t)blockIdx.x * S + split) * kOut : nullptr;
+  for (int o = tid; o < kOut; o += kThreads) {
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) sum += red[w * kOut + o];
+    if (S == 1)
+      store(o, sum);
+    else  // agent-coherent store: straight to the point all XCDs see
+      __hip_atomic_store(mine + o, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (S == 1) return;
+  // K-splits: the last split of this tile group to finish adds all S partial
+  // tiles in split order (the same bits whichever finishes last) and re-arms the
+  // group's counter for the next call.  Partials are written and read with
+  // agent-coherent accesses, so no cache of any XCD has to be written back or
+  // dropped; the stores are complete (vmcnt 0) before the counter moves, and the
+  // reads are issued only by the workgroup that saw the final count.
+  __shared__ int last;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's partial stores are done
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev =
+        __hip_atomic_fetch_add(cnt + blockIdx.x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = prev == (uint32_t)(S - 1);
+    if (last) __hip_atomic_store(cnt + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!last) return;
+  const float *const all = part + (int64_t)blockIdx.x * S * kOut;
+  for (int o = tid; o < kOut; o += kThreads) {
+    float sum = __hip_atomic_load(all + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int q = 1; q < S; ++q)
+      sum += __hip_atomic_load(all + (int64_t)q * kOut + o, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    store(o, sum);
   }
 }
 
@@ -434,29 +471,58 @@ hipError_t go(const uint8_t *codes, const uint16_t *scales, int N, int K, const 
 
 template <int MT, int TB>
 hipError_t go_pair(const uint8_t *codes, const uint16_t *scales, int N, int K, const uint16_t *X,
-                   int M, float *Y, hipStream_t stream) {
+                   int M, float *Y, int S, uint32_t *cnt, float *part, hipStream_t stream) {
   constexpr int D = 1;  // pairs in flight per wave (measured: deeper rings run slower)
   const int tiles = (N + 15) / 16;
   const int blocks = (tiles + TB - 1) / TB;
-  hipLaunchKernelGGL((gemm_mfma_pair_kernel<MT, TB, D>), dim3(blocks), dim3(kThreads), 0, stream,
-                     codes, scales, X, Y, N, K, M);
+  hipLaunchKernelGGL((gemm_mfma_pair_kernel<MT, TB, D>), dim3(blocks, S), dim3(kThreads), 0,
+                     stream, codes, scales, X, Y, N, K, M, S, cnt, part);
   return hipGetLastError();
 }
 
 template <int MT>
 hipError_t go_pair_tb(int TB, const uint8_t *codes, const uint16_t *scales, int N, int K,
-                      const uint16_t *X, int M, float *Y, hipStream_t s) {
+                      const uint16_t *X, int M, float *Y, int S, uint32_t *cnt, float *part,
+                      hipStream_t s) {
   switch (TB) {
-    case 1: return go_pair<MT, 1>(codes, scales, N, K, X, M, Y, s);
-    case 2: return go_pair<MT, 2>(codes, scales, N, K, X, M, Y, s);
-    case 3: return go_pair<MT, 3>(codes, scales, N, K, X, M, Y, s);
-    case 4: return go_pair<MT, 4>(codes, scales, N, K, X, M, Y, s);
-    case 5: return go_pair<MT, 5>(codes, scales, N, K, X, M, Y, s);
-    // (MT = 2 with 6 tiles spills registers at one step in flight; 7 does not)
-    case 6: return go_pair<MT, MT == 2 ? 7 : 6>(codes, scales, N, K, X, M, Y, s);
-    case 7: return go_pair<MT, 7>(codes, scales, N, K, X, M, Y, s);
-    default: return go_pair<MT, 8>(codes, scales, N, K, X, M, Y, s);
+    case 1: return go_pair<MT, 1>(codes, scales, N, K, X, M, Y, S, cnt, part, s);
+    case 2: return go_pair<MT, 2>(codes, scales, N, K, X, M, Y, S, cnt, part, s);
+    case 3: return go_pair<MT, 3>(codes, scales, N, K, X, M, Y, S, cnt, part, s);
+    case 4: return go_pair<MT, 4>(codes, scales, N, K, X, M, Y, S, cnt, part, s);
+    case 5: return go_pair<MT, 5>(codes, scales, N, K, X, M, Y, S, cnt, part, s);
+    // (never chosen for MT = 2, whose 6-tile form spills registers)
+    case 6: return go_pair<MT, MT == 2 ? 7 : 6>(codes, scales, N, K, X, M, Y, S, cnt, part, s);
+    case 7: return go_pair<MT, 7>(codes, scales, N, K, X, M, Y, S, cnt, part, s);
+    default: return go_pair<MT, 8>(codes, scales, N, K, X, M, Y, S, cnt, part, s);
   }
+}
+
+// Pair-step plan: TB column tiles per workgroup and S K-splits.  Without a
+// workspace, S = 1 and TB just gives every CU a workgroup.  With one, K is split
+// only where it measured faster: two 16-row tiles (M > 16), one column tile per
+// CU and at least 64 pair steps (8192 of K) -- there four tiles per workgroup
+// share each activation fragment in four K-splits (Llama-3.1-8B down projection
+// at M = 32: 38.0 -> 28.0 us).  Elsewhere the wider tiles and shorter K-ranges
+// lose more to set-up and to the partial-tile traffic than they save.
+struct PairPlan {
+  int TB, S;
+};
+
+PairPlan plan_pair(int N, int K, int M, bool split) {
+  const int NT = (N + 15) / 16;
+  const int NP = (K >> 6) >> 1;
+  PairPlan p{std::min((NT + kCUs - 1) / kCUs, 8), 1};
+  if (M > 16 && p.TB == 6) p.TB = 7;  // the 6-tile form spills registers at MT = 2
+  if (split && M > 16 && p.TB == 1 && NP >= 64) p = PairPlan{4, 4};
+  return p;
+}
+
+int64_t pair_workspace_bytes(int N, int M, const PairPlan &p) {
+  if (p.S == 1) return 0;
+  const int MT = M <= 16 ? 1 : 2;
+  const int64_t groups = ((N + 15) / 16 + p.TB - 1) / p.TB;
+  const int64_t counters = (groups * 4 + 255) / 256 * 256;
+  return counters + groups * p.S * p.TB * MT * 256 * 4;
 }
 
 template <int MT>
@@ -476,21 +542,38 @@ hipError_t go_tb(int TB, const uint8_t *codes, const uint16_t *scales, int N, in
 
 }  // namespace
 
+int64_t gemm_mfma_workspace_bytes(int64_t N, int64_t K, int M) {
+  if (M < 1 || M > 32 || (K >> 6) % 2 != 0) return 0;
+  return pair_workspace_bytes((int)N, M, plan_pair((int)N, (int)K, M, true));
+}
+
 hipError_t launch_gemm_mfma(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
-                            const uint16_t *X, int M, float *Y, hipStream_t stream) {
+                            const uint16_t *X, int M, float *Y, void *workspace,
+                            int64_t workspace_bytes, hipStream_t stream) {
   if (M < 1 || M > 32) return hipErrorInvalidValue;
   const int n = (int)N, k = (int)K;
-  // column tiles per workgroup: enough for one workgroup per CU, at most 8
-  // (past that, workgroups run in rounds)
-  const int tiles = (n + 15) / 16;
-  const int TB = std::min((tiles + kCUs - 1) / kCUs, 8);
   // pair steps need an even group count and 4-byte aligned scales (every model
   // shape); otherwise one group per step
   const bool pair = ((k >> 6) % 2 == 0) && ((reinterpret_cast<uintptr_t>(scales) & 3) == 0);
   if (pair) {
-    if (M <= 16) return go_pair_tb<1>(TB, codes, scales, n, k, X, M, Y, stream);
-    return go_pair_tb<2>(TB, codes, scales, n, k, X, M, Y, stream);
+    PairPlan p = plan_pair(n, k, M, workspace != nullptr);
+    uint32_t *cnt = nullptr;
+    float *part = nullptr;
+    if (p.S > 1) {
+      const int64_t need = pair_workspace_bytes(n, M, p);
+      if (workspace_bytes < need) return hipErrorInvalidValue;
+      const int64_t groups = ((n + 15) / 16 + p.TB - 1) / p.TB;
+      cnt = static_cast<uint32_t *>(workspace);
+      part = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                       (groups * 4 + 255) / 256 * 256);
+    }
+    if (M <= 16) return go_pair_tb<1>(p.TB, codes, scales, n, k, X, M, Y, p.S, cnt, part, stream);
+    return go_pair_tb<2>(p.TB, codes, scales, n, k, X, M, Y, p.S, cnt, part, stream);
   }
+  // column tiles per workgroup: enough for one workgroup per CU, at most 8
+  // (past that, workgroups run in rounds)
+  const int tiles = (n + 15) / 16;
+  const int TB = std::min((tiles + kCUs - 1) / kCUs, 8);
   if (M <= 16) return go_tb<1>(TB, codes, scales, n, k, X, M, Y, stream);
   return go_tb<2>(TB, codes, scales, n, k, X, M, Y, stream);
 }

@@ -15,9 +15,13 @@ hipError_t launch_unpack(const uint8_t *codes, const uint16_t *scales, int64_t N
 hipError_t launch_gemv_valu(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
                             const uint16_t *X, int M, float *Y, hipStream_t stream);
 
-// MFMA product, 8 <= M <= 32.
+// MFMA product, 8 <= M <= 32.  With a workspace (workspace_bytes at least
+// gemm_mfma_workspace_bytes, its counter area zero before first use), K may be
+// split over workgroups; without one (nullptr), never.
 hipError_t launch_gemm_mfma(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
-                            const uint16_t *X, int M, float *Y, hipStream_t stream);
+                            const uint16_t *X, int M, float *Y, void *workspace,
+                            int64_t workspace_bytes, hipStream_t stream);
+int64_t gemm_mfma_workspace_bytes(int64_t N, int64_t K, int M);
 
 // MFMA product with 64 x 64 .. 128 x 128 workgroup tiles, any M >= 1 (prefill).
 hipError_t launch_gemm_prefill(const uint8_t *codes, const uint16_t *scales, int64_t N,

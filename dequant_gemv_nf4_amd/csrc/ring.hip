@@ -122,7 +122,7 @@ int nf4_ring_gemm(nf4_ring *r, const uint8_t *host_codes, const uint16_t *host_s
   const int m = (int)M;
   hipError_t le = (m < 8 && nf4::valu_supported(N, K, m))
                       ? nf4::launch_gemv_valu(codes, scales, N, K, X, m, Y, r->compute)
-                      : nf4::launch_gemm_mfma(codes, scales, N, K, X, m, Y, r->compute);
+                      : nf4::launch_gemm_mfma(codes, scales, N, K, X, m, Y, nullptr, 0, r->compute);
   if (int e = fail(le)) return e;
   if (int e = fail(hipEventRecord(r->read_done[s], r->compute))) return e;
   r->used[s] = true;

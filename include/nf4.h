@@ -116,6 +116,31 @@ int nf4_gemm_smallm(const uint8_t *codes, const uint16_t *scales, int64_t N, int
                     const uint16_t *X, int64_t M, float *Y, void *stream);
 
 /*
+ * nf4_gemm_smallm_ws -- nf4_gemm_smallm with a caller-owned device workspace
+ * that lets the MFMA kernel split K over workgroups (wider column tiles share
+ * each activation fragment while every CU still gets work).  Each split writes
+ * its partial tile to the workspace; the last split of a tile group to finish
+ * adds the partials in split order, so results are deterministic (they may
+ * differ in the last bits from nf4_gemm_smallm, whose sums are grouped
+ * differently; both meet the stated tolerance).
+ *  - workspace: device memory, 256-byte aligned, at least
+ *    nf4_gemm_smallm_workspace_bytes(N, K, M) bytes (0 bytes: the call is
+ *    nf4_gemm_smallm and workspace may be NULL).  Its first bytes are counters
+ *    that must be zero before the workspace's first use; every completed call
+ *    leaves them zero again, so one zero-fill at allocation suffices.  Calls
+ *    that share a workspace must not run concurrently (e.g. use one per stream).
+ *  - Errors: as nf4_gemm_smallm; NF4_ERANGE if the workspace is missing or too
+ *    small; NF4_EALIGN if it is not 256-byte aligned.
+ * Source: deep-fold README, "Method" (prompt chunks of up to 32 positions).
+ * nf4_gemm_smallm_workspace_bytes: the bytes needed for (N, K, M), 0 if the
+ * call would not split, -1 if the shape or M is invalid.  Host only.
+ */
+int64_t nf4_gemm_smallm_workspace_bytes(int64_t N, int64_t K, int64_t M);
+int nf4_gemm_smallm_ws(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                       const uint16_t *X, int64_t M, float *Y, void *workspace,
+                       int64_t workspace_bytes, void *stream);
+
+/*
  * nf4_gemm_prefill -- the same product, Y[m][n] = sum_k L[code(n,k)] *
  * s(n,k/64) * X[m][k], for any batch 1 <= M with M * K < 2^30 (prefill chunks
  * beyond 32 positions), on 32 x 32 x 16 bf16 MFMA tiles of 64 x 64 to 128 x 128

@@ -33,6 +33,9 @@ def lib():
     L.nf4_gemv.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     L.nf4_gemm_smallm.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp]
     L.nf4_gemm_prefill.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp]
+    L.nf4_gemm_smallm_ws.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, i64, vp]
+    L.nf4_gemm_smallm_workspace_bytes.argtypes = [i64, i64, i64]
+    L.nf4_gemm_smallm_workspace_bytes.restype = ctypes.c_int64
     L.nf4_embed.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, vp]
     L.nf4_ring_create.argtypes = [ctypes.POINTER(ctypes.c_void_p), vp, vp, i64, vp, vp]
     L.nf4_ring_gemm.argtypes = [vp, vp, vp, i64, i64, vp, i64, vp]
@@ -46,6 +49,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = _declared()
     for required in ("nf4_pack", "nf4_unpack", "nf4_gemv", "nf4_gemm_smallm", "nf4_gemm_prefill",
+                     "nf4_gemm_smallm_ws", "nf4_gemm_smallm_workspace_bytes",
                      "nf4_embed",
                      "nf4_ring_create", "nf4_ring_gemm", "nf4_ring_slot_bytes", "nf4_ring_destroy",
                      "nf4_codebook", "nf4_strerror"):
@@ -111,6 +115,29 @@ def test_prefill_null_and_alignment(lib):
     assert lib.nf4_gemm_prefill(P, ctypes.c_void_p(0x100001), 4, 64, P, 64, P, NULL) == EALIGN
     assert lib.nf4_gemm_prefill(P, P, 4, 64, P_ODD, 64, P, NULL) == EALIGN
     assert lib.nf4_gemm_prefill(P, P, 4, 64, P, 64, P_ODD, NULL) == EALIGN
+
+
+def test_smallm_workspace_sizes(lib):
+    wb = lib.nf4_gemm_smallm_workspace_bytes
+    assert wb(0, 64, 8) == -1 and wb(4, 100, 8) == -1 and wb(4, 64, 0) == -1 and wb(4, 64, 33) == -1
+    assert wb(4096, 4096, 4) == 0          # vector-ALU path: never splits
+    assert wb(28672, 4096, 32) == 0        # enough column tiles for every CU
+    assert wb(4096, 4096, 32) == 0         # too short a K to split
+    assert wb(4096, 14336, 8) == 0         # one 16-row tile: splitting does not pay
+    assert wb(4096, 14336, 32) > 0 and wb(4096, 14336, 32) % 256 == 0
+    assert wb(33, 320, 8) == 0
+
+
+def test_smallm_ws_validation(lib):
+    W = ctypes.c_void_p(0x200000)
+    need = lib.nf4_gemm_smallm_workspace_bytes(4096, 14336, 32)
+    # a split shape without (enough) workspace, or a misaligned one, is refused
+    assert lib.nf4_gemm_smallm_ws(P, P, 4096, 14336, P, 32, P, NULL, 0, NULL) == ERANGE
+    assert lib.nf4_gemm_smallm_ws(P, P, 4096, 14336, P, 32, P, W, need - 1, NULL) == ERANGE
+    assert lib.nf4_gemm_smallm_ws(P, P, 4096, 14336, P, 32, P, ctypes.c_void_p(0x200010),
+                                  need, NULL) == EALIGN
+    assert lib.nf4_gemm_smallm_ws(P, P, 4096, 14336, P, 40, P, W, need, NULL) == ERANGE
+    assert lib.nf4_gemm_smallm_ws(NULL, P, 4096, 14336, P, 32, P, W, need, NULL) == EINVAL
 
 
 def test_alignment(lib):
