@@ -366,8 +366,8 @@ def main():
     # one workspace for the small-batch products that split K over workgroups:
     # every launch runs on one stream after the previous, and each call leaves
     # the workspace's counters re-armed
-    ws_bytes = max([nf4.smallm_workspace_bytes(N, K, M) for _, N, K, *_ in items]
-                   if 1 < M <= nf4.MAX_M else [0])
+    wsize = nf4.smallm_workspace_bytes if M <= nf4.MAX_M else nf4.prefill_workspace_bytes
+    ws_bytes = max([wsize(N, K, M) for _, N, K, *_ in items]) if M > 1 else 0
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
 
     def launch(it):
@@ -377,7 +377,7 @@ def main():
         elif M <= nf4.MAX_M:
             nf4.nf4_gemm_smallm_ws(codes, scales, X, Y, ws)
         else:
-            nf4.nf4_gemm_prefill(codes, scales, X, Y)
+            nf4.nf4_gemm_prefill_ws(codes, scales, X, Y, ws)
 
     def sweep():
         for it in items:

@@ -27,12 +27,14 @@ from ._lib import (  # noqa: F401
     nf4_codebook,
     nf4_embed,
     nf4_gemm_prefill,
+    nf4_gemm_prefill_ws,
     nf4_gemm_smallm,
     nf4_gemm_smallm_ws,
     nf4_gemv,
     nf4_pack,
     nf4_unpack,
     pack,
+    prefill_workspace_bytes,
     ring_slot_bytes,
     smallm_workspace_bytes,
     unpack,

@@ -49,6 +49,9 @@ def _load():
     L.nf4_gemm_smallm_ws.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, i64, vp]
     L.nf4_gemm_smallm_workspace_bytes.argtypes = [i64, i64, i64]
     L.nf4_gemm_smallm_workspace_bytes.restype = ctypes.c_int64
+    L.nf4_gemm_prefill_ws.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, i64, vp]
+    L.nf4_gemm_prefill_workspace_bytes.argtypes = [i64, i64, i64]
+    L.nf4_gemm_prefill_workspace_bytes.restype = ctypes.c_int64
     L.nf4_embed.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, vp]
     L.nf4_ring_create.argtypes = [ctypes.POINTER(ctypes.c_void_p), vp, vp, i64, vp, vp]
     L.nf4_ring_gemm.argtypes = [vp, vp, vp, i64, i64, vp, i64, vp]
@@ -58,7 +61,7 @@ def _load():
     for f in (L.nf4_ring_create, L.nf4_ring_gemm, L.nf4_ring_destroy):
         f.restype = ctypes.c_int
     for f in (L.nf4_pack, L.nf4_unpack, L.nf4_gemv, L.nf4_gemm_smallm, L.nf4_gemm_smallm_ws,
-              L.nf4_gemm_prefill, L.nf4_embed):
+              L.nf4_gemm_prefill, L.nf4_gemm_prefill_ws, L.nf4_embed):
         f.restype = ctypes.c_int
     L.nf4_codebook.argtypes = [ctypes.POINTER(ctypes.c_float)]
     L.nf4_codebook.restype = None
@@ -227,6 +230,35 @@ def nf4_gemm_prefill(codes, scales, X, Y, stream=None):
                                                             _stream(X.device, stream)))
 
 
+def prefill_workspace_bytes(N, K, M):
+    """Bytes of workspace nf4_gemm_prefill_ws needs for (N, K, M); 0 = no split."""
+    n = _load().nf4_gemm_prefill_workspace_bytes(int(N), int(K), int(M))
+    if n < 0:
+        raise ValueError(f"invalid shape N={N} K={K} M={M}")
+    return int(n)
+
+
+def nf4_gemm_prefill_ws(codes, scales, X, Y, workspace, stream=None):
+    """nf4_gemm_prefill with a device workspace (uint8 tensor, counters zeroed
+    before its first use; or None when prefill_workspace_bytes is 0)."""
+    _need(codes, "codes", (torch.uint8,), (2,))
+    _need(scales, "scales", _U16 + (torch.float16,))
+    _need(X, "X", _BF16, (1, 2))
+    _need(Y, "Y", (torch.float32,))
+    M, K = (1, X.shape[0]) if X.dim() == 1 else X.shape
+    N = _nk(codes, scales, K)
+    if Y.numel() != M * N:
+        raise ValueError("Y must have M*N elements")
+    nbytes = 0
+    if workspace is not None:
+        _need(workspace, "workspace", (torch.uint8,))
+        nbytes = workspace.numel()
+    with torch.cuda.device(X.device):
+        _check("nf4_gemm_prefill_ws", _load().nf4_gemm_prefill_ws(
+            _ptr(codes), _ptr(scales), N, K, _ptr(X), M, _ptr(Y), _ptr(workspace), nbytes,
+            _stream(X.device, stream)))
+
+
 def nf4_embed(codes, scales, K, ids, out, dev_status=None, stream=None):
     """out bf16 [T][K] = rows ids (int64 [T]) of dequant(codes, scales), rounded once."""
     _need(codes, "codes", (torch.uint8,), (2,))
@@ -358,5 +390,9 @@ def gemm(codes, scales, X, stream=None):
         else:
             nf4_gemm_smallm(codes, scales, X, Y, stream)
     else:
-        nf4_gemm_prefill(codes, scales, X, Y, stream)
+        need = prefill_workspace_bytes(codes.shape[0], X.shape[-1], M)
+        if need:
+            nf4_gemm_prefill_ws(codes, scales, X, Y, workspace_for(X.device, need, stream), stream)
+        else:
+            nf4_gemm_prefill(codes, scales, X, Y, stream)
     return Y

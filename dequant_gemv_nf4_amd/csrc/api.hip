@@ -113,6 +113,28 @@ int nf4_gemm_smallm(const uint8_t *codes, const uint16_t *scales, int64_t N, int
   return launched(nf4::launch_gemm_mfma(codes, scales, N, K, X, m, Y, nullptr, 0, s));
 }
 
+int64_t nf4_gemm_prefill_workspace_bytes(int64_t N, int64_t K, int64_t M) {
+  if (check_shape(N, K) || M < 1 || M * K >= (int64_t(1) << 30)) return -1;
+  return nf4::gemm_prefill_workspace_bytes(N, K, M);
+}
+
+int nf4_gemm_prefill_ws(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                        const uint16_t *X, int64_t M, float *Y, void *workspace,
+                        int64_t workspace_bytes, void *stream) {
+  if (!codes || !scales || !X || !Y) return NF4_EINVAL;
+  if (int r = check_shape(N, K)) return r;
+  if (M < 1 || M * K >= (int64_t(1) << 30)) return NF4_ERANGE;  // X below 2 GiB
+  if (!aligned(codes, 16) || !aligned(scales, 2) || !aligned(X, 16) || !aligned(Y, 4) ||
+      (workspace && !aligned(workspace, 256)))
+    return NF4_EALIGN;
+  const int64_t need = nf4::gemm_prefill_workspace_bytes(N, K, M);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return NF4_ERANGE;
+  if (int r = check_device()) return r;
+  return launched(nf4::launch_gemm_prefill(codes, scales, N, K, X, M, Y,
+                                           need > 0 ? workspace : nullptr, workspace_bytes,
+                                           (hipStream_t)stream));
+}
+
 int nf4_gemm_prefill(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
                      const uint16_t *X, int64_t M, float *Y, void *stream) {
   if (!codes || !scales || !X || !Y) return NF4_EINVAL;
@@ -122,7 +144,7 @@ int nf4_gemm_prefill(const uint8_t *codes, const uint16_t *scales, int64_t N, in
     return NF4_EALIGN;
   if (int r = check_device()) return r;
   return launched(
-      nf4::launch_gemm_prefill(codes, scales, N, K, X, M, Y, (hipStream_t)stream));
+      nf4::launch_gemm_prefill(codes, scales, N, K, X, M, Y, nullptr, 0, (hipStream_t)stream));
 }
 
 int nf4_gemv(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,

@@ -114,7 +114,7 @@ template <int RM, int CN, int P, int KS>
 __global__ void __launch_bounds__(kPThreads * KS)
     gemm_prefill_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
                         const uint16_t *__restrict__ X, float *__restrict__ Y, int N, int K,
-                        int M) {
+                        int M, int S, uint32_t *__restrict__ cnt, float *__restrict__ partial) {
   constexpr int BM = 64 * RM;
   constexpr int kXChunks = BM * 8 / kPThreads;  // 16-byte activation chunks per thread
   constexpr int kStage = BM * kXRow;            // bytes of one activation buffer
@@ -132,7 +132,11 @@ __global__ void __launch_bounds__(kPThreads * KS)
   const int wr = (wave >> 1) & 1, wc = wave & 1;
   const int col = lane & 31, h = lane >> 5;
   const int NG = K >> 6;
-  const int nsteps = (NG + KS - 1) / KS;  // the same for every split (barriers match)
+  // workgroup K-split blockIdx.z of S takes the groups [g0, g0 + ng)
+  const int zs = blockIdx.z;
+  const int g0 = (int)((int64_t)zs * NG / S);
+  const int ng = (int)((int64_t)(zs + 1) * NG / S) - g0;
+  const int nsteps = (ng + KS - 1) / KS;  // the same for every split (barriers match)
   const int m0 = blockIdx.y * BM;
   const int n0 = blockIdx.x * (64 * CN);
   // this split's activation stages [2][BM][kXRow]
@@ -165,7 +169,7 @@ __global__ void __launch_bounds__(kPThreads * KS)
   u32x4_t cr[P][CN];
   uint32_t sr[P][CN];
   auto group_of = [&](int j) __attribute__((always_inline)) {
-    return __builtin_amdgcn_readfirstlane(min(KS * j + split, NG - 1));
+    return __builtin_amdgcn_readfirstlane(g0 + min(KS * j + split, ng - 1));
   };
   auto load_x = [&](auto slot, int j) __attribute__((always_inline)) {
     constexpr int d = decltype(slot)::value;
@@ -204,7 +208,7 @@ __global__ void __launch_bounds__(kPThreads * KS)
     __syncthreads();
     load_x(slot, j + P);
     // the last step of a split with fewer groups only keeps the barriers in step
-    if (KS == 1 || KS * j + split < NG) {
+    if (KS * j + split < ng) {
       f32x16_t t[RM][CN];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -298,20 +302,65 @@ __global__ void __launch_bounds__(kPThreads * KS)
               acc[r][c][i] += red[(((wq * RM + r) * CN + c) * 16 + i) * 64 + lane];
       }
     }
-    if (split != 0) return;
   }
 
+  constexpr int BN = 64 * CN;
+  if (S == 1) {
+    if (split != 0) return;
 #pragma unroll
-  for (int r = 0; r < RM; ++r)
+    for (int r = 0; r < RM; ++r)
 #pragma unroll
-    for (int c = 0; c < CN; ++c) {
-      const int n = n0 + 32 * CN * wc + 32 * c + col;
+      for (int c = 0; c < CN; ++c) {
+        const int n = n0 + 32 * CN * wc + 32 * c + col;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int m = m0 + 32 * RM * wr + 32 * r + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (m < M && n < N) Y[(int64_t)m * N + n] = acc[r][c][i];
+        for (int i = 0; i < 16; ++i) {
+          const int m = m0 + 32 * RM * wr + 32 * r + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (m < M && n < N) Y[(int64_t)m * N + n] = acc[r][c][i];
+        }
       }
-    }
+    return;
+  }
+  // Workgroup K-splits: split 0 of each writes its tile to the workspace with
+  // agent-coherent stores; the last of the S workgroups of this tile to finish
+  // (a counter per tile, re-armed by that workgroup) adds the S tiles in split
+  // order, so the bits do not depend on which finishes last.
+  const int64_t tile = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  if (split == 0) {
+    float *const mine = partial + (tile * S + zs) * (BM * BN);
+#pragma unroll
+    for (int r = 0; r < RM; ++r)
+#pragma unroll
+      for (int c = 0; c < CN; ++c) {
+        const int nl = 32 * CN * wc + 32 * c + col;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ml = 32 * RM * wr + 32 * r + 8 * (i >> 2) + 4 * h + (i & 3);
+          __hip_atomic_store(mine + ml * BN + nl, acc[r][c][i], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+  }
+  __shared__ int last;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores are done
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev =
+        __hip_atomic_fetch_add(cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = prev == (uint32_t)(S - 1);
+    if (last) __hip_atomic_store(cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!last) return;
+  const float *const all = partial + tile * S * (BM * BN);
+  for (int e = tid; e < BM * BN; e += kPThreads * KS) {
+    const int m = m0 + e / BN, n = n0 + e % BN;
+    if (m >= M || n >= N) continue;
+    float sum = __hip_atomic_load(all + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int q = 1; q < S; ++q)
+      sum += __hip_atomic_load(all + (int64_t)q * (BM * BN) + e, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    Y[(int64_t)m * N + n] = sum;
+  }
 }
 
 namespace {
@@ -322,27 +371,71 @@ constexpr int kCUs = 256;
 
 template <int RM, int CN, int P, int KS>
 hipError_t go_prefill(const uint8_t *codes, const uint16_t *scales, int N, int K,
-                      const uint16_t *X, int M, float *Y, hipStream_t stream) {
-  const dim3 grid(cdiv(N, 64 * CN), cdiv(M, 64 * RM));
+                      const uint16_t *X, int M, float *Y, int S, uint32_t *cnt, float *partial,
+                      hipStream_t stream) {
+  const dim3 grid(cdiv(N, 64 * CN), cdiv(M, 64 * RM), S);
   hipLaunchKernelGGL((gemm_prefill_kernel<RM, CN, P, KS>), grid, dim3(kPThreads * KS), 0, stream,
-                     codes, scales, X, Y, N, K, M);
+                     codes, scales, X, Y, N, K, M, S, cnt, partial);
   return hipGetLastError();
+}
+
+// Workgroup tile (64 RM x 64 CN), in-workgroup K-splits KS and workgroup
+// K-splits S.  The tile is the largest of 128 x 128, 64 x 128, 64 x 64 that
+// still gives every CU a workgroup, else the smallest (128 x 64 is never needed:
+// 64 x 128 gives at least as many workgroups).  P (steps in flight, even: the
+// LDS stage alternates) and KS are as large as the registers allow.  With a
+// workspace, a grid of fewer than 256 workgroups is multiplied by the largest S
+// that keeps it within 256 (and at least two steps per wave).
+struct PrefillPlan {
+  int RM, CN, KS, S;
+  int64_t tiles;
+};
+
+PrefillPlan plan_prefill(int n, int k, int m, bool split) {
+  auto blocks = [&](int bm, int bn) { return (int64_t)cdiv(n, bn) * cdiv(m, bm); };
+  PrefillPlan p;
+  if (blocks(128, 128) >= kCUs)
+    p = PrefillPlan{2, 2, 2, 1, blocks(128, 128)};
+  else if (blocks(64, 128) >= kCUs)
+    p = PrefillPlan{1, 2, 2, 1, blocks(64, 128)};
+  else
+    p = PrefillPlan{1, 1, 4, 1, blocks(64, 64)};
+  if (split && p.tiles < kCUs) {
+    // whole rounds only: a second, partial round of workgroups costs more than
+    // the split saves (measured on q|k|v at M = 128)
+    const int smax = (k >> 6) / (2 * p.KS);
+    p.S = std::max(1, std::min((int)(kCUs / p.tiles), smax));
+  }
+  return p;
+}
+
+int64_t prefill_workspace_bytes(const PrefillPlan &p) {
+  if (p.S == 1) return 0;
+  return (p.tiles * 4 + 255) / 256 * 256 + p.tiles * p.S * (64 * p.RM) * (64 * p.CN) * 4;
 }
 
 }  // namespace
 
+int64_t gemm_prefill_workspace_bytes(int64_t N, int64_t K, int64_t M) {
+  return prefill_workspace_bytes(plan_prefill((int)N, (int)K, (int)M, true));
+}
+
 hipError_t launch_gemm_prefill(const uint8_t *codes, const uint16_t *scales, int64_t N,
-                               int64_t K, const uint16_t *X, int64_t M, float *Y,
-                               hipStream_t stream) {
+                               int64_t K, const uint16_t *X, int64_t M, float *Y, void *workspace,
+                               int64_t workspace_bytes, hipStream_t stream) {
   const int n = (int)N, k = (int)K, m = (int)M;
-  // the largest tile that still gives every CU a workgroup, else the smallest
-  // (128 x 64 is never needed: 64 x 128 gives at least as many workgroups)
-  auto blocks = [&](int bm, int bn) { return (int64_t)cdiv(n, bn) * cdiv(m, bm); };
-  // P = steps in flight per split (even: the LDS stage alternates), KS = K-splits
-  // of 4 waves; both as large as the registers allow (256 per lane at 8 waves)
-  if (blocks(128, 128) >= kCUs) return go_prefill<2, 2, 2, 2>(codes, scales, n, k, X, m, Y, stream);
-  if (blocks(64, 128) >= kCUs) return go_prefill<1, 2, 2, 2>(codes, scales, n, k, X, m, Y, stream);
-  return go_prefill<1, 1, 2, 4>(codes, scales, n, k, X, m, Y, stream);
+  const PrefillPlan p = plan_prefill(n, k, m, workspace != nullptr);
+  uint32_t *cnt = nullptr;
+  float *partial = nullptr;
+  if (p.S > 1) {
+    if (workspace_bytes < prefill_workspace_bytes(p)) return hipErrorInvalidValue;
+    cnt = static_cast<uint32_t *>(workspace);
+    partial = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                        (p.tiles * 4 + 255) / 256 * 256);
+  }
+  if (p.RM == 2) return go_prefill<2, 2, 2, 2>(codes, scales, n, k, X, m, Y, p.S, cnt, partial, stream);
+  if (p.CN == 2) return go_prefill<1, 2, 2, 2>(codes, scales, n, k, X, m, Y, p.S, cnt, partial, stream);
+  return go_prefill<1, 1, 2, 4>(codes, scales, n, k, X, m, Y, p.S, cnt, partial, stream);
 }
 
 }  // namespace nf4

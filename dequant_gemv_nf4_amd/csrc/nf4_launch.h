@@ -23,10 +23,12 @@ hipError_t launch_gemm_mfma(const uint8_t *codes, const uint16_t *scales, int64_
                             int64_t workspace_bytes, hipStream_t stream);
 int64_t gemm_mfma_workspace_bytes(int64_t N, int64_t K, int M);
 
-// MFMA product with 64 x 64 .. 128 x 128 workgroup tiles, any M >= 1 (prefill).
+// MFMA product with 64 x 64 .. 128 x 128 workgroup tiles, any M >= 1 (prefill);
+// with a workspace (as for launch_gemm_mfma), small grids split K over workgroups.
 hipError_t launch_gemm_prefill(const uint8_t *codes, const uint16_t *scales, int64_t N,
-                               int64_t K, const uint16_t *X, int64_t M, float *Y,
-                               hipStream_t stream);
+                               int64_t K, const uint16_t *X, int64_t M, float *Y, void *workspace,
+                               int64_t workspace_bytes, hipStream_t stream);
+int64_t gemm_prefill_workspace_bytes(int64_t N, int64_t K, int64_t M);
 
 // Packed embedding rows into bf16; status (may be null) is cleared first.
 hipError_t launch_embed(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,

@@ -153,6 +153,24 @@ int nf4_gemm_smallm_ws(const uint8_t *codes, const uint16_t *scales, int64_t N, 
 int nf4_gemm_prefill(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
                      const uint16_t *X, int64_t M, float *Y, void *stream);
 
+/*
+ * nf4_gemm_prefill_ws -- nf4_gemm_prefill with a caller-owned device workspace
+ * that lets a grid of fewer output tiles than CUs split K over workgroups (each
+ * tile's S partial tiles are added in split order by the last to finish:
+ * deterministic; bits may differ from nf4_gemm_prefill's, both within the
+ * tolerance).  Workspace rules as for nf4_gemm_smallm_ws: 256-byte aligned, at
+ * least nf4_gemm_prefill_workspace_bytes(N, K, M) bytes (0: no split, NULL
+ * allowed), counters zero before first use and re-armed by every completed call,
+ * no concurrent calls sharing one.  Errors: as nf4_gemm_prefill; NF4_ERANGE for
+ * a missing or short workspace, NF4_EALIGN for a misaligned one.
+ * Source: deep-fold README, "Method" (prefill on the NF4 matrix-core product).
+ * nf4_gemm_prefill_workspace_bytes: bytes needed (0: no split), -1 if invalid.
+ */
+int64_t nf4_gemm_prefill_workspace_bytes(int64_t N, int64_t K, int64_t M);
+int nf4_gemm_prefill_ws(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                        const uint16_t *X, int64_t M, float *Y, void *workspace,
+                        int64_t workspace_bytes, void *stream);
+
 /* bit OR-ed into *dev_status by nf4_embed */
 #define NF4_EMBED_BAD_ID 1 /* an id outside [0, N): its output row is all +0 */
 

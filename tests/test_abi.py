@@ -36,6 +36,9 @@ def lib():
     L.nf4_gemm_smallm_ws.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, i64, vp]
     L.nf4_gemm_smallm_workspace_bytes.argtypes = [i64, i64, i64]
     L.nf4_gemm_smallm_workspace_bytes.restype = ctypes.c_int64
+    L.nf4_gemm_prefill_ws.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, i64, vp]
+    L.nf4_gemm_prefill_workspace_bytes.argtypes = [i64, i64, i64]
+    L.nf4_gemm_prefill_workspace_bytes.restype = ctypes.c_int64
     L.nf4_embed.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, vp]
     L.nf4_ring_create.argtypes = [ctypes.POINTER(ctypes.c_void_p), vp, vp, i64, vp, vp]
     L.nf4_ring_gemm.argtypes = [vp, vp, vp, i64, i64, vp, i64, vp]
@@ -50,6 +53,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for required in ("nf4_pack", "nf4_unpack", "nf4_gemv", "nf4_gemm_smallm", "nf4_gemm_prefill",
                      "nf4_gemm_smallm_ws", "nf4_gemm_smallm_workspace_bytes",
+                     "nf4_gemm_prefill_ws", "nf4_gemm_prefill_workspace_bytes",
                      "nf4_embed",
                      "nf4_ring_create", "nf4_ring_gemm", "nf4_ring_slot_bytes", "nf4_ring_destroy",
                      "nf4_codebook", "nf4_strerror"):
@@ -138,6 +142,20 @@ def test_smallm_ws_validation(lib):
                                   need, NULL) == EALIGN
     assert lib.nf4_gemm_smallm_ws(P, P, 4096, 14336, P, 40, P, W, need, NULL) == ERANGE
     assert lib.nf4_gemm_smallm_ws(NULL, P, 4096, 14336, P, 32, P, W, need, NULL) == EINVAL
+
+
+def test_prefill_workspace_sizes_and_validation(lib):
+    wb = lib.nf4_gemm_prefill_workspace_bytes
+    assert wb(0, 64, 64) == -1 and wb(4, 64, 0) == -1 and wb(4, 2 ** 15, 2 ** 15) == -1
+    assert wb(4096, 4096, 512) == 0 and wb(1000, 576, 64) == 0
+    need = wb(4096, 4096, 64)
+    assert need > 0 and need % 256 == 0
+    W = ctypes.c_void_p(0x200000)
+    assert lib.nf4_gemm_prefill_ws(P, P, 4096, 4096, P, 64, P, NULL, 0, NULL) == ERANGE
+    assert lib.nf4_gemm_prefill_ws(P, P, 4096, 4096, P, 64, P, W, need - 1, NULL) == ERANGE
+    assert lib.nf4_gemm_prefill_ws(P, P, 4096, 4096, P, 64, P, ctypes.c_void_p(0x200010),
+                                   need, NULL) == EALIGN
+    assert lib.nf4_gemm_prefill_ws(P, P, 4096, 4096, P, 0, P, W, need, NULL) == ERANGE
 
 
 def test_alignment(lib):

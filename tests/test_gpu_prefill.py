@@ -155,13 +155,16 @@ def test_prefill_scales_only_2_byte_aligned(nf4):
 
 
 def test_gemm_dispatches_beyond_32_rows(nf4):
-    """nf4.gemm routes M > 32 to the prefill tiles: same bits as nf4_gemm_prefill."""
+    """nf4.gemm routes M > 32 to the prefill tiles (with a kept workspace where
+    the grid splits K): the same bits as the direct calls."""
     N, K = 128, 512
     codes, scales = _pack(nf4, wl.weights(N, K, 0.02, seed=31, device=DEV))
     X = wl.activations(48, K, seed=32, device=DEV)
+    need = nf4.prefill_workspace_bytes(N, K, 48)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=DEV)
     Y = nf4.gemm(codes, scales, X)
     torch.cuda.synchronize()
-    assert torch.equal(Y, _prefill(nf4, codes, scales, X))
+    assert torch.equal(Y, _prefill_ws(nf4, codes, scales, X, ws if need else None))
 
 
 @pytest.mark.parametrize("M", [64, 512])
@@ -177,3 +180,65 @@ def test_prefill_full_size_8b(nf4, M):
             seen.add((N, K))
             _case(nf4, M, N, K, seed=wl.seed_for(set_.name, 0, name, "W") % 100000,
                   rows=_rows(N, 32, N + K + M))
+
+
+# ------------------------------------------------------------------ workgroup K-splits
+def _prefill_ws(nf4, codes, scales, X, ws):
+    Y = torch.empty((X.shape[0], codes.shape[0]), dtype=torch.float32, device=X.device)
+    nf4.nf4_gemm_prefill_ws(codes, scales, X, Y, ws)
+    torch.cuda.synchronize()
+    return Y
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 4096, 4096), (100, 300, 2048), (70, 129, 8192),
+                                   (33, 64, 4160), (128, 6144, 4096), (64, 1000, 576)])
+def test_prefill_split_matches_oracle_and_repeats(nf4, M, N, K):
+    need = nf4.prefill_workspace_bytes(N, K, M)
+    W = wl.weights(N, K, 0.02, seed=N * 3 + K + M, device=DEV)
+    X = wl.activations(M, K, seed=N + K * 5 + M, device=DEV)
+    codes, scales = _pack(nf4, W)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=DEV)
+    Y1 = _prefill_ws(nf4, codes, scales, X, ws)
+    Y2 = _prefill_ws(nf4, codes, scales, X, ws)
+    Y3 = _prefill_ws(nf4, codes, scales, X, ws)
+    # the same bits on every call: the counters re-arm after each one
+    assert torch.equal(Y1, Y2) and torch.equal(Y1, Y3)
+    rows = _rows(N, 64, M + N) if N * K > 2 ** 22 else np.arange(N)
+    r = torch.from_numpy(rows).to(DEV)
+    ref_p, ref_s, _ = oracle.quantize_pack(W[r].cpu().numpy())
+    Yr, A = oracle.gemm(ref_p, ref_s, wl.bf16_bits(X))
+    _check(Y1[:, r], Yr, A, f"prefill split M={M} N={N} K={K}")
+    Y0 = _prefill(nf4, codes, scales, X)
+    _check(Y0[:, r], Yr, A, f"prefill unsplit M={M} N={N} K={K}")
+
+
+def test_prefill_split_planned_for_small_grids(nf4):
+    assert nf4.prefill_workspace_bytes(4096, 4096, 64) > 0
+    assert nf4.prefill_workspace_bytes(300, 2048, 100) > 0
+    assert nf4.prefill_workspace_bytes(1000, 576, 64) == 0      # too few groups to split
+    assert nf4.prefill_workspace_bytes(28672, 4096, 64) == 0    # grid already fills the CUs
+    assert nf4.prefill_workspace_bytes(4096, 4096, 512) == 0
+
+
+def test_prefill_split_in_a_hip_graph(nf4):
+    N, K, M = 4096, 4096, 64
+    codes, scales = _pack(nf4, wl.weights(N, K, 0.02, seed=95, device=DEV))
+    X = wl.activations(M, K, seed=96, device=DEV)
+    ws = torch.zeros(nf4.prefill_workspace_bytes(N, K, M), dtype=torch.uint8, device=DEV)
+    ref = _prefill_ws(nf4, codes, scales, X, ws)
+    Y = torch.zeros_like(ref)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        nf4.nf4_gemm_prefill_ws(codes, scales, X, Y, ws)
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        nf4.nf4_gemm_prefill_ws(codes, scales, X, Y, ws)
+    for i in range(4):
+        Y.zero_()
+        _ = _prefill_ws(nf4, codes, scales, X, ws)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y, ref), i
