@@ -8,7 +8,6 @@
 #include "nf4_launch.h"
 
 namespace nf4 {
-bool valu_supported(int64_t N, int64_t K, int M);
 }
 
 namespace {
@@ -71,7 +70,7 @@ int nf4_unpack(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t 
 
 int64_t nf4_gemm_smallm_workspace_bytes(int64_t N, int64_t K, int64_t M) {
   if (check_shape(N, K) || M < 1 || M > NF4_MAX_M) return -1;
-  if (M < 8 && nf4::valu_supported(N, K, (int)M)) return 0;
+  if (nf4::use_valu(N, K, (int)M)) return 0;
   return nf4::gemm_mfma_workspace_bytes(N, K, (int)M);
 }
 
@@ -89,10 +88,7 @@ int nf4_gemm_smallm_ws(const uint8_t *codes, const uint16_t *scales, int64_t N, 
   if (int r = check_device()) return r;
   const int m = (int)M;
   hipStream_t s = (hipStream_t)stream;
-  // M < 8 on the vector ALUs (decode shared across the M dot products); the
-  // batch tiles from 8 rows up, and the rare small-M shapes whose activations do
-  // not fit the VALU kernel's registers, on MFMA.
-  if (m < 8 && nf4::valu_supported(N, K, m))
+  if (nf4::use_valu(N, K, m))
     return launched(nf4::launch_gemv_valu(codes, scales, N, K, X, m, Y, s));
   return launched(nf4::launch_gemm_mfma(codes, scales, N, K, X, m, Y,
                                         need > 0 ? workspace : nullptr, workspace_bytes, s));
@@ -108,7 +104,7 @@ int nf4_gemm_smallm(const uint8_t *codes, const uint16_t *scales, int64_t N, int
   if (int r = check_device()) return r;
   const int m = (int)M;
   hipStream_t s = (hipStream_t)stream;
-  if (m < 8 && nf4::valu_supported(N, K, m))
+  if (nf4::use_valu(N, K, m))
     return launched(nf4::launch_gemv_valu(codes, scales, N, K, X, m, Y, s));
   return launched(nf4::launch_gemm_mfma(codes, scales, N, K, X, m, Y, nullptr, 0, s));
 }

@@ -11,9 +11,20 @@ hipError_t launch_pack(const float *W, int64_t N, int64_t K, uint8_t *codes, uin
 hipError_t launch_unpack(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
                          float *out, hipStream_t stream);
 
-// VALU product, 1 <= M <= 7 (the GEMV is M = 1).
+// VALU product, 1 <= M <= 7 (the GEMV is M = 1), for the shapes its plan fits.
 hipError_t launch_gemv_valu(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
                             const uint16_t *X, int M, float *Y, hipStream_t stream);
+bool valu_supported(int64_t N, int64_t K, int M);
+
+// Which kernel a batch of M rows runs on: the vector-ALU kernel (one weight
+// decode shared by M dot products) for M <= 3, and for M = 4 on matrices wider
+// than 8192 rows; the MFMA kernel otherwise.  Measured on the Llama-3.1-8B
+// shapes: MFMA wins from M = 5 everywhere and at M = 4 on the 4096- and
+// 6144-row matrices (4096x4096: 6.6 vs 8.4 us), VALU at M = 4 on 28672 rows
+// (24.4 vs 32.4 us) and below.
+inline bool use_valu(int64_t N, int64_t K, int M) {
+  return (M <= 3 || (M == 4 && N > 8192)) && valu_supported(N, K, M);
+}
 
 // MFMA product, 8 <= M <= 32.  With a workspace (workspace_bytes at least
 // gemm_mfma_workspace_bytes, its counter area zero before first use), K may be

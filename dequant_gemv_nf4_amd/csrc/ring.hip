@@ -18,7 +18,6 @@
 #include "nf4_launch.h"
 
 namespace nf4 {
-bool valu_supported(int64_t N, int64_t K, int M);
 int device_status();  // NF4_OK on a gfx950 device (api.hip)
 }
 
@@ -120,7 +119,7 @@ int nf4_ring_gemm(nf4_ring *r, const uint8_t *host_codes, const uint16_t *host_s
   if (int e = fail(hipEventRecord(r->copied[s], r->copy))) return e;
   if (int e = fail(hipStreamWaitEvent(r->compute, r->copied[s], 0))) return e;
   const int m = (int)M;
-  hipError_t le = (m < 8 && nf4::valu_supported(N, K, m))
+  hipError_t le = nf4::use_valu(N, K, m)
                       ? nf4::launch_gemv_valu(codes, scales, N, K, X, m, Y, r->compute)
                       : nf4::launch_gemm_mfma(codes, scales, N, K, X, m, Y, nullptr, 0, r->compute);
   if (int e = fail(le)) return e;

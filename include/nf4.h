@@ -35,10 +35,11 @@
  * memory is touched.  Asynchronous GPU faults surface on the stream as usual.
  *
  * Numerics: nf4_pack and nf4_unpack are exact (bit-for-bit defined below).
- * The products accumulate in fp32.  Below M = 8 the levels are f16 and each
- * activation block is scaled by a power of two into f16; from M = 8 (and in
- * nf4_gemm_prefill) the levels are split into bf16 hi + lo and the bf16
- * activations are used as they are.  Per output element
+ * The products accumulate in fp32.  On the vector-ALU kernel (M <= 3, and
+ * M = 4 on matrices wider than 8192 rows) the levels are f16 and each
+ * activation block is scaled by a power of two into f16; on the MFMA kernels
+ * (every other M, and nf4_gemm_prefill) the levels are split into bf16 hi + lo
+ * and the bf16 activations are used as they are.  Per output element
  * |Y - Y_exact| <= 2e-3 * sum_k |w~(n,k) X[m][k]| + 1e-5 for finite inputs whose
  * products stay in range.  Results are deterministic: the same call on the same
  * device gives the same bits.
@@ -109,7 +110,8 @@ int nf4_gemv(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
  * nf4_gemm_smallm -- Y[m][n] = sum_k L[code(n,k)] * s(n,k/64) * X[m][k] for
  * 1 <= M <= 32 (prefill chunks, speculative verification batches).
  * Source: deep-fold README, "Method" (prompt chunks of up to 32 positions on a
- * tensor-core NF4 GEMM).  M = 1 is the GEMV; M >= 8 runs on MFMA.
+ * tensor-core NF4 GEMM).  M = 1 is the GEMV; from M = 5 (M = 4 on matrices of
+ * up to 8192 rows) the product runs on MFMA.
  * Alignment: codes 16 bytes, scales 2, X 16, Y 4.
  */
 int nf4_gemm_smallm(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
