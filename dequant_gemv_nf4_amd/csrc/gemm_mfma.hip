@@ -34,6 +34,12 @@
 // groups; every load is unconditional (past-the-end groups and tiles re-read a
 // valid address), so waits are exact.  The 8 partial tiles are summed in LDS in
 // wave order: deterministic, no atomics.
+//
+// The pair-step kernel (two groups per step, gemm_mfma_pair_kernel) is the one
+// every model shape uses; with a caller workspace it can also split K over S
+// workgroups per tile group (blockIdx.y), whose partial tiles meet in the
+// workspace and are added in split order by the last to finish (see
+// plan_pair for where that pays).
 #include <utility>
 
 #include "nf4_device.h"
