@@ -1,7 +1,9 @@
 """Build libnf4.so (HIP, gfx950) in-tree with hipcc.
 
 One shared library holds every kernel and the C ABI of include/nf4.h.  Packed
-FP32 instructions are switched off for all device code.
+FP32 instructions are switched off for all device code.  Kernel arguments are
+preloaded into scalar registers (up to 14 words, gfx950 supports it), so a wave
+does not wait on an argument load before its first memory requests.
 """
 import os
 import subprocess
@@ -18,6 +20,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 def command(out: str):
     return [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-kernarg-preload-count=16",
             "-I", os.path.join(ROOT, "include"), "-Wall",
             "-o", out] + [os.path.join(CSRC, s) for s in SOURCES]
 

@@ -64,8 +64,11 @@ constexpr int kXChunks = (kStageBytes / kUnitStageBytes * 4 + kThreads - 1) / kT
 template <int M, int UPL, bool WS>
 __global__ void __launch_bounds__(kThreads)
     gemv_valu_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
-                     const uint16_t *__restrict__ X, float *__restrict__ Y, int N, int K, int S,
-                     int G, int Us, int iters) {
+                     const uint16_t *__restrict__ X, float *__restrict__ Y, int N, int K,
+                     int sgu, int iters, int nblocks) {
+  // (13 argument words in all, so that every one arrives preloaded in scalar
+  // registers: no argument load sits between a wave's start and its first loads)
+  const int S = sgu & 15, G = (sgu >> 4) & 15, Us = sgu >> 8;
   // rows of codes in flight per wave (registers).  Two for M = 1: measured
   // deeper rings run slower, since a wave whose next load waits for room at the
   // address unit cannot go on to compute rows whose data has arrived.
@@ -90,7 +93,7 @@ __global__ void __launch_bounds__(kThreads)
   // rows are dealt round-robin over the grid: step t of group g of workgroup b
   // handles row (t * blocks + b) * G + g
   const int row0 = blockIdx.x * G;
-  const int rstride = gridDim.x * G;
+  const int rstride = nblocks * G;
   const int64_t row_bytes = K >> 1;
   const int64_t row_groups = K >> 6;
 
@@ -131,9 +134,6 @@ __global__ void __launch_bounds__(kThreads)
   // chunks; chunk c is quarter c % 4 of unit (c / 4) % U of row c / (4 U).
   // Threads past the end load the last chunk again (no branch around loads).
   const int nchunks = M * U * 4;
-  // The decode table goes first: it needs no memory, and built later it would
-  // queue behind the loads for the address unit.
-  build_byte_lut(lut, tid, kThreads);
 
   // A wave issues only the chunk loads it needs (the branch is uniform per wave).
   uint4 xr[kXChunks];
@@ -189,6 +189,9 @@ __global__ void __launch_bounds__(kThreads)
     load_row(d, row0 + grp + d * rstride, row_first, cb[d], sb[d]);
     __builtin_amdgcn_sched_barrier(0);
   }
+  // The decode table is built while the first rows are in flight: it needs no
+  // memory, and the code rows, with the longest wait, go out first.
+  build_byte_lut(lut, tid, kThreads);
 
   // ---- activations: convert, stage, copy into registers.  Each unit is scaled
   // by its own power of two (the largest |x| of its 32 values, a max over the 4
@@ -397,10 +400,10 @@ hipError_t go(const Plan &p, const uint8_t *codes, const uint16_t *scales, int N
   const bool ws = ((K >> 6) % 2 == 0) && ((reinterpret_cast<uintptr_t>(scales) & 3) == 0);
   if (ws)
     hipLaunchKernelGGL((gemv_valu_kernel<M, UPL, true>), dim3(p.blocks), dim3(kThreads), 0, stream,
-                       codes, scales, X, Y, N, K, p.S, p.G, p.Us, p.iters);
+                       codes, scales, X, Y, N, K, p.S | p.G << 4 | p.Us << 8, p.iters, p.blocks);
   else
     hipLaunchKernelGGL((gemv_valu_kernel<M, UPL, false>), dim3(p.blocks), dim3(kThreads), 0, stream,
-                       codes, scales, X, Y, N, K, p.S, p.G, p.Us, p.iters);
+                       codes, scales, X, Y, N, K, p.S | p.G << 4 | p.Us << 8, p.iters, p.blocks);
   return hipGetLastError();
 }
 
