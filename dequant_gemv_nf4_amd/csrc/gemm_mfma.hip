@@ -262,7 +262,7 @@ template <int MT, int TB, int D>
 __global__ void __launch_bounds__(kThreads)
     gemm_mfma_pair_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
                           const uint16_t *__restrict__ X, float *__restrict__ Y, int N, int K,
-                          int M, int S, uint32_t *__restrict__ cnt, float *__restrict__ part) {
+                          int M, int S, uint32_t *__restrict__ cnt) {
   constexpr int kRedWords = kWaves * TB * MT * 4 * 64;
   constexpr int kLdsWords = kRedWords > kLutWords ? kRedWords : kLutWords;
   __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsWords];
@@ -275,6 +275,12 @@ __global__ void __launch_bounds__(kThreads)
   const int NP = NG >> 1;  // pairs per row
   const int NT = (N + 15) >> 4;
   const int t0 = blockIdx.x * TB;
+  // the workspace: one counter per tile group, then (256-byte aligned) the
+  // partial tiles (derived here, so that every argument fits the preloaded
+  // argument registers)
+  float *const part = S > 1 ? reinterpret_cast<float *>(reinterpret_cast<char *>(cnt) +
+                                                         (((NT + TB - 1) / TB) * 4 + 255) / 256 * 256)
+                            : nullptr;
   // K-split blockIdx.y of S takes the pair steps [p0, p0 + np)
   const int split = blockIdx.y;
   const int p0 = (int)((int64_t)split * NP / S);
@@ -482,7 +488,8 @@ hipError_t go_pair(const uint8_t *codes, const uint16_t *scales, int N, int K, c
   const int tiles = (N + 15) / 16;
   const int blocks = (tiles + TB - 1) / TB;
   hipLaunchKernelGGL((gemm_mfma_pair_kernel<MT, TB, D>), dim3(blocks, S), dim3(kThreads), 0,
-                     stream, codes, scales, X, Y, N, K, M, S, cnt, part);
+                     stream, codes, scales, X, Y, N, K, M, S, cnt);
+  (void)part;  // the kernel derives the same address from cnt
   return hipGetLastError();
 }
 

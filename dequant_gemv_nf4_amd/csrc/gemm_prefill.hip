@@ -114,7 +114,7 @@ template <int RM, int CN, int P, int KS>
 __global__ void __launch_bounds__(kPThreads * KS)
     gemm_prefill_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
                         const uint16_t *__restrict__ X, float *__restrict__ Y, int N, int K,
-                        int M, int S, uint32_t *__restrict__ cnt, float *__restrict__ partial) {
+                        int M, int S, uint32_t *__restrict__ cnt) {
   constexpr int BM = 64 * RM;
   constexpr int kXChunks = BM * 8 / kPThreads;  // 16-byte activation chunks per thread
   constexpr int kStage = BM * kXRow;            // bytes of one activation buffer
@@ -324,7 +324,14 @@ __global__ void __launch_bounds__(kPThreads * KS)
   // agent-coherent stores; the last of the S workgroups of this tile to finish
   // (a counter per tile, re-armed by that workgroup) adds the S tiles in split
   // order, so the bits do not depend on which finishes last.
-  const int64_t tile = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  // the workspace: one counter per output tile, then (256-byte aligned) the
+  // partial tiles; both derived from the shape, so that every argument fits the
+  // preloaded argument registers
+  const int tiles_n = (N + BN - 1) / BN;
+  const int64_t tiles = (int64_t)tiles_n * ((M + BM - 1) / BM);
+  float *const partial =
+      reinterpret_cast<float *>(reinterpret_cast<char *>(cnt) + (tiles * 4 + 255) / 256 * 256);
+  const int64_t tile = (int64_t)blockIdx.y * tiles_n + blockIdx.x;
   if (split == 0) {
     float *const mine = partial + (tile * S + zs) * (BM * BN);
 #pragma unroll
@@ -375,7 +382,8 @@ hipError_t go_prefill(const uint8_t *codes, const uint16_t *scales, int N, int K
                       hipStream_t stream) {
   const dim3 grid(cdiv(N, 64 * CN), cdiv(M, 64 * RM), S);
   hipLaunchKernelGGL((gemm_prefill_kernel<RM, CN, P, KS>), grid, dim3(kPThreads * KS), 0, stream,
-                     codes, scales, X, Y, N, K, M, S, cnt, partial);
+                     codes, scales, X, Y, N, K, M, S, cnt);
+  (void)partial;  // the kernel derives the same address from cnt
   return hipGetLastError();
 }
 
