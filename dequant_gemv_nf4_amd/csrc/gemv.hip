@@ -254,7 +254,7 @@ __global__ void __launch_bounds__(kThreads)
     }
 
   // ---- rows
-  const uint32_t laneoff = (uint32_t)lane * 4u;
+  const uint32_t laneoff = lut_lane_offset(lane);
   auto compute_row = [&](int r, int step, const uint4 *c, const ScaleT *s) {
     float acc[M];
 #pragma unroll

@@ -42,44 +42,52 @@ constexpr LevelF16 kLevelF16 = make_level_f16();
 // Entry for a packed byte b holds the two f16 levels of its nibbles:
 //   low half  = L[b & 15]  (even k),  high half = L[b >> 4]  (odd k),
 // i.e. exactly the operand pair of one v_dot2_f32_f16 against (x[2j], x[2j+1]).
-// Each entry is replicated 64 times, 4 bytes apart, so that lane l reads copy l:
-// byte address = b * 256 + 4 * lane.  Every lane then hits its own bank whatever
-// the codes are, and the address is one v_perm_b32 from the code word.
+// Each entry is replicated 32 times, 4 bytes apart, at a 256-byte stride: lane l
+// reads copy l % 32 at byte address b * 256 + 4 * (l % 32).  LDS serves a 32-bit
+// read in two halves of 32 lanes, and within a half every lane hits its own bank
+// whatever the codes are (measured: no slower than 64 copies, and half the
+// table writes).  The address is one v_perm_b32 from the code word.  The upper
+// 128 bytes of each 256-byte row are not written.
 // ---------------------------------------------------------------------------
-constexpr int kLutWords = 256 * 64;  // 64 KiB
+constexpr int kLutWords = 256 * 64;  // 64 KiB of addresses, 32 KiB written
 
 // Wave w writes the entries whose high nibble h satisfies h % nwaves == w: for
-// one h that is 16 entries x 64 copies = 256 uint4 stores, 4 per lane.  Store
-// (h, j, lane) covers entry 16h + 4j + lane/16, so the high level is a constant
-// of the unrolled loop and the low level a 4-way choice fixed per lane.
+// one h that is 16 entries x 32 copies = 128 uint4 stores, 2 per lane.  Store
+// (h, j, lane) covers copies 4 (lane % 8) .. + 3 of entry 16h + 8j + lane/8, so
+// the high level is a constant of the unrolled loop and the low level an
+// 8-way choice fixed per lane.
 __device__ __forceinline__ void build_byte_lut(uint32_t *lut, int tid, int nthreads) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nwaves = nthreads >> 6;
-  const uint32_t sub = (uint32_t)lane >> 4;
-  uint32_t lo[4];
+  const uint32_t sub = (uint32_t)lane >> 3;
+  uint32_t lo[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t a = kLevelF16.v[4 * j + 0], b = kLevelF16.v[4 * j + 1];
-    const uint32_t c = kLevelF16.v[4 * j + 2], d = kLevelF16.v[4 * j + 3];
-    lo[j] = sub == 0 ? a : (sub == 1 ? b : (sub == 2 ? c : d));
+  for (int j = 0; j < 2; ++j) {
+    uint32_t v = kLevelF16.v[8 * j];
+#pragma unroll
+    for (int q = 1; q < 8; ++q) v = sub == (uint32_t)q ? kLevelF16.v[8 * j + q] : v;
+    lo[j] = v;
   }
   uint4 *L4 = reinterpret_cast<uint4 *>(lut);
 #pragma unroll
   for (int h = 0; h < 16; ++h) {
     if (h % nwaves == wave) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 2; ++j) {
         const uint32_t e = lo[j] | (kLevelF16.v[h] << 16);
-        L4[h * 256 + j * 64 + lane] = make_uint4(e, e, e, e);
+        L4[(16 * h + 8 * j + sub) * 16 + (lane & 7)] = make_uint4(e, e, e, e);
       }
     }
   }
 }
 
+// lane offset into an entry: copy lane % 32
+__device__ __forceinline__ uint32_t lut_lane_offset(int lane) { return (uint32_t)(lane & 31) * 4u; }
+
 // selector for v_perm_b32: result byte0 = lane offset (low byte of src1),
 // byte1 = byte `j` of the code word (src0), bytes 2..3 = 0
-//   -> (code_byte_j << 8) | (4 * lane)
+//   -> (code_byte_j << 8) | (4 * (lane % 32))
 template <int j>
 __device__ __forceinline__ uint32_t lut_addr(uint32_t codeword, uint32_t laneoff) {
   constexpr uint32_t sel = 0x0c0c0000u | ((4u + j) << 8) | 0x00u;
