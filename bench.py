@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16 / bf16 matrix cores, published
 METRIC = "NF4 GEMV effective HBM GB/s and % of peak at M=1; µs/layer-set (7B shapes)"
+INFINITY_CACHE_BYTES = 256 << 20  # MI355X last-level (MALL) cache
 
 
 def parse():
@@ -522,7 +523,10 @@ def main():
                                 "same-x projections fused along N (q|k|v, gate|up)"),
                    "m": M, "packed_gb": round(packed_bytes / 1e9, 3),
                    "step_algorithmic_mb": round(step_bytes / 1e6, 3),
-                   "timing": "hip-graph replay" if graph is not None else "eager launches"},
+                   "timing": "hip-graph replay" if graph is not None else "eager launches",
+                   "cache": ("cold: weights rotate through more than the 256 MB infinity cache"
+                             if packed_bytes > INFINITY_CACHE_BYTES else
+                             "warm: all weights fit the 256 MB infinity cache")},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "us_per_layer_set": round(ms_per_step * 1e3 / L, 3),
         "kernel_us_per_layer_set": round(kernel_sum_us / L, 3),
