@@ -431,7 +431,9 @@ def main():
     order = [name for name, _ in groups_]
     for proj in order:
         its = [it for it in items if it[0] == proj]
-        nl = max(1, min(args.event_launches, 4 * len(its)))
+        # (a set with one layer repeats its matrix: enough launches that the
+        # graph's own launch cost is spread thin)
+        nl = max(1, args.event_launches if len(its) < 4 else min(args.event_launches, 4 * len(its)))
         g = torch.cuda.CUDAGraph()
         s2 = torch.cuda.Stream()
         s2.wait_stream(torch.cuda.current_stream())
