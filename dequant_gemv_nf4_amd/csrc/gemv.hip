@@ -18,7 +18,10 @@
 // fixed registers, so the address unit gets no per-row vector arithmetic.  A
 // short ring of rows per wave keeps the next loads in flight; no load sits behind
 // a branch and no register a load in flight reads is rewritten early, so the
-// compiler's waits cover exactly the row being consumed.
+// compiler's waits cover exactly the row being consumed.  Order of the set-up:
+// activation loads, the first code rows, then the decode table (built while the
+// rows are in flight), then the activation staging.  All kernel arguments fit
+// the preloaded argument registers, so nothing waits on an argument load.
 //
 // Decode: one v_perm_b32 turns a code byte into the LDS address of its entry in
 // the bank-replicated byte table (nf4_device.h); the entry is the f16 pair
