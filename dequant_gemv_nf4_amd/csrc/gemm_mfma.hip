@@ -275,12 +275,11 @@ __global__ void __launch_bounds__(kThreads)
   const int NP = NG >> 1;  // pairs per row
   const int NT = (N + 15) >> 4;
   const int t0 = blockIdx.x * TB;
-  // the workspace: one counter per tile group, then (256-byte aligned) the
-  // partial tiles (derived here, so that every argument fits the preloaded
-  // argument registers)
-  float *const part = S > 1 ? reinterpret_cast<float *>(reinterpret_cast<char *>(cnt) +
-                                                         (((NT + TB - 1) / TB) * 4 + 255) / 256 * 256)
-                            : nullptr;
+  // the workspace: the counter area, then the partial tiles (the address is
+  // derived here, so that every argument fits the preloaded argument registers)
+  float *const part =
+      S > 1 ? reinterpret_cast<float *>(reinterpret_cast<char *>(cnt) + kSplitCounterBytes)
+            : nullptr;
   // K-split blockIdx.y of S takes the pair steps [p0, p0 + np)
   const int split = blockIdx.y;
   const int p0 = (int)((int64_t)split * NP / S);
@@ -512,11 +511,17 @@ hipError_t go_pair_tb(int TB, const uint8_t *codes, const uint16_t *scales, int 
 
 // Pair-step plan: TB column tiles per workgroup and S K-splits.  Without a
 // workspace, S = 1 and TB just gives every CU a workgroup.  With one, K is split
-// only where it measured faster: two 16-row tiles (M > 16), one column tile per
-// CU and at least 64 pair steps (8192 of K) -- there four tiles per workgroup
-// share each activation fragment in four K-splits (Llama-3.1-8B down projection
-// at M = 32: 38.0 -> 28.0 us).  Elsewhere the wider tiles and shorter K-ranges
-// lose more to set-up and to the partial-tile traffic than they save.
+// where a sweep of (TB, S) over the Llama-3.1-8B shapes measured it faster:
+//  - one column tile per CU, two 16-row tiles (M > 16): four tiles in four
+//    K-splits from 8192 of K (down: 38.0 -> 27.6 us at M = 32), else two in two
+//    (4096 x 4096: 14.2 -> 13.5 us);
+//  - one column tile per CU, M of 5 to 16, 8192 of K or more: two tiles in two
+//    K-splits (down 4096 x 14336: M = 16 22.9 -> 19.8 us, M = 8 18.2 -> 17.4);
+//  - two column tiles per workgroup (fewer workgroups than CUs), M > 16: three
+//    tiles in two K-splits, which fills every CU (q|k|v 6144 x 4096 at M = 32:
+//    17.8 -> 16.2 us).
+// Elsewhere (M <= 4, K = 4096 at M <= 16, the wide gate|up tiles) the shorter
+// K-ranges lose more to set-up and to the partial-tile traffic than they save.
 struct PairPlan {
   int TB, S;
 };
@@ -526,7 +531,10 @@ PairPlan plan_pair(int N, int K, int M, bool split) {
   const int NP = (K >> 6) >> 1;
   PairPlan p{std::min((NT + kCUs - 1) / kCUs, 8), 1};
   if (M > 16 && p.TB == 6) p.TB = 7;  // the 6-tile form spills registers at MT = 2
-  if (split && M > 16 && p.TB == 1 && NP >= 64) p = PairPlan{4, 4};
+  if (!split || NP < 16 || NT > kSplitCounters) return p;
+  if (p.TB == 1 && M > 16) p = NP >= 64 ? PairPlan{4, 4} : PairPlan{2, 2};
+  else if (p.TB == 1 && M > 4 && NP >= 64) p = PairPlan{2, 2};
+  else if (p.TB == 2 && M > 16) p = PairPlan{3, 2};
   return p;
 }
 
@@ -534,8 +542,7 @@ int64_t pair_workspace_bytes(int N, int M, const PairPlan &p) {
   if (p.S == 1) return 0;
   const int MT = M <= 16 ? 1 : 2;
   const int64_t groups = ((N + 15) / 16 + p.TB - 1) / p.TB;
-  const int64_t counters = (groups * 4 + 255) / 256 * 256;
-  return counters + groups * p.S * p.TB * MT * 256 * 4;
+  return kSplitCounterBytes + groups * p.S * p.TB * MT * 256 * 4;
 }
 
 template <int MT>
@@ -575,10 +582,8 @@ hipError_t launch_gemm_mfma(const uint8_t *codes, const uint16_t *scales, int64_
     if (p.S > 1) {
       const int64_t need = pair_workspace_bytes(n, M, p);
       if (workspace_bytes < need) return hipErrorInvalidValue;
-      const int64_t groups = ((n + 15) / 16 + p.TB - 1) / p.TB;
       cnt = static_cast<uint32_t *>(workspace);
-      part = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                       (groups * 4 + 255) / 256 * 256);
+      part = reinterpret_cast<float *>(static_cast<char *>(workspace) + kSplitCounterBytes);
     }
     if (M <= 16) return go_pair_tb<1>(p.TB, codes, scales, n, k, X, M, Y, p.S, cnt, part, stream);
     return go_pair_tb<2>(p.TB, codes, scales, n, k, X, M, Y, p.S, cnt, part, stream);

@@ -324,13 +324,11 @@ __global__ void __launch_bounds__(kPThreads * KS)
   // agent-coherent stores; the last of the S workgroups of this tile to finish
   // (a counter per tile, re-armed by that workgroup) adds the S tiles in split
   // order, so the bits do not depend on which finishes last.
-  // the workspace: one counter per output tile, then (256-byte aligned) the
-  // partial tiles; both derived from the shape, so that every argument fits the
-  // preloaded argument registers
+  // the workspace: the counter area, then the partial tiles (the address and the
+  // tile index are derived here, so that every argument fits the preloaded
+  // argument registers)
   const int tiles_n = (N + BN - 1) / BN;
-  const int64_t tiles = (int64_t)tiles_n * ((M + BM - 1) / BM);
-  float *const partial =
-      reinterpret_cast<float *>(reinterpret_cast<char *>(cnt) + (tiles * 4 + 255) / 256 * 256);
+  float *const partial = reinterpret_cast<float *>(reinterpret_cast<char *>(cnt) + kSplitCounterBytes);
   const int64_t tile = (int64_t)blockIdx.y * tiles_n + blockIdx.x;
   if (split == 0) {
     float *const mine = partial + (tile * S + zs) * (BM * BN);
@@ -419,7 +417,7 @@ PrefillPlan plan_prefill(int n, int k, int m, bool split) {
 
 int64_t prefill_workspace_bytes(const PrefillPlan &p) {
   if (p.S == 1) return 0;
-  return (p.tiles * 4 + 255) / 256 * 256 + p.tiles * p.S * (64 * p.RM) * (64 * p.CN) * 4;
+  return kSplitCounterBytes + (int64_t)p.tiles * p.S * (64 * p.RM) * (64 * p.CN) * 4;
 }
 
 }  // namespace
@@ -438,8 +436,7 @@ hipError_t launch_gemm_prefill(const uint8_t *codes, const uint16_t *scales, int
   if (p.S > 1) {
     if (workspace_bytes < prefill_workspace_bytes(p)) return hipErrorInvalidValue;
     cnt = static_cast<uint32_t *>(workspace);
-    partial = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                        (p.tiles * 4 + 255) / 256 * 256);
+    partial = reinterpret_cast<float *>(static_cast<char *>(workspace) + kSplitCounterBytes);
   }
   if (p.RM == 2) return go_prefill<2, 2, 2, 2>(codes, scales, n, k, X, m, Y, p.S, cnt, partial, stream);
   if (p.CN == 2) return go_prefill<1, 2, 2, 2>(codes, scales, n, k, X, m, Y, p.S, cnt, partial, stream);

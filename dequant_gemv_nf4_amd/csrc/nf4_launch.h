@@ -26,6 +26,14 @@ inline bool use_valu(int64_t N, int64_t K, int M) {
   return (M <= 3 || (M == 4 && N > 8192)) && valu_supported(N, K, M);
 }
 
+// Workspace layout of every K-splitting call (small-batch and prefill): the
+// first kSplitCounterBytes hold one 32-bit counter per tile group (at most
+// kSplitCounters groups split), the partial tiles start right after.  The
+// counter area has the same place and size for every shape, and each call
+// leaves its counters zero, so one workspace serves calls of any shape in turn.
+constexpr int kSplitCounters = 1024;
+constexpr int kSplitCounterBytes = kSplitCounters * 4;
+
 // MFMA product, 8 <= M <= 32.  With a workspace (workspace_bytes at least
 // gemm_mfma_workspace_bytes, its counter area zero before first use), K may be
 // split over workgroups; without one (nullptr), never.

@@ -127,10 +127,13 @@ int nf4_gemm_smallm(const uint8_t *codes, const uint16_t *scales, int64_t N, int
  * differently; both meet the stated tolerance).
  *  - workspace: device memory, 256-byte aligned, at least
  *    nf4_gemm_smallm_workspace_bytes(N, K, M) bytes (0 bytes: the call is
- *    nf4_gemm_smallm and workspace may be NULL).  Its first bytes are counters
+ *    nf4_gemm_smallm and workspace may be NULL).  Its first 4 KiB are counters
  *    that must be zero before the workspace's first use; every completed call
- *    leaves them zero again, so one zero-fill at allocation suffices.  Calls
- *    that share a workspace must not run concurrently (e.g. use one per stream).
+ *    leaves them zero again, so one zero-fill at allocation suffices.  The
+ *    counter area has the same place and size for every shape (partial tiles
+ *    follow it), so one workspace serves calls of any shapes, of this function
+ *    and of nf4_gemm_prefill_ws, one after another.  Calls that share a
+ *    workspace must not run concurrently (e.g. use one per stream).
  *  - Errors: as nf4_gemm_smallm; NF4_ERANGE if the workspace is missing or too
  *    small; NF4_EALIGN if it is not 256-byte aligned.
  * Source: deep-fold README, "Method" (prompt chunks of up to 32 positions).
@@ -162,7 +165,8 @@ int nf4_gemm_prefill(const uint8_t *codes, const uint16_t *scales, int64_t N, in
  * deterministic; bits may differ from nf4_gemm_prefill's, both within the
  * tolerance).  Workspace rules as for nf4_gemm_smallm_ws: 256-byte aligned, at
  * least nf4_gemm_prefill_workspace_bytes(N, K, M) bytes (0: no split, NULL
- * allowed), counters zero before first use and re-armed by every completed call,
+ * allowed), the same 4 KiB counter area (zero before first use, re-armed by
+ * every completed call; shareable with nf4_gemm_smallm_ws calls of any shape),
  * no concurrent calls sharing one.  Errors: as nf4_gemm_prefill; NF4_ERANGE for
  * a missing or short workspace, NF4_EALIGN for a misaligned one.
  * Source: deep-fold README, "Method" (prefill on the NF4 matrix-core product).

@@ -126,9 +126,13 @@ def test_smallm_workspace_sizes(lib):
     assert wb(0, 64, 8) == -1 and wb(4, 100, 8) == -1 and wb(4, 64, 0) == -1 and wb(4, 64, 33) == -1
     assert wb(4096, 4096, 4) == 0          # vector-ALU path: never splits
     assert wb(28672, 4096, 32) == 0        # enough column tiles for every CU
-    assert wb(4096, 4096, 32) == 0         # too short a K to split
-    assert wb(4096, 14336, 8) == 0         # one 16-row tile: splitting does not pay
+    assert wb(4096, 4096, 16) == 0         # K = 4096 at M <= 16: splitting does not pay
+    assert wb(4096, 14336, 4) == 0         # M = 4 on the matrix cores: neither
+    assert wb(4096, 4096, 32) > 0          # one tile per CU at M > 16: two splits
+    assert wb(6144, 4096, 32) > 0          # fewer workgroups than CUs: three tiles, two splits
+    assert wb(4096, 14336, 8) > 0          # long K from M = 5: two tiles, two splits
     assert wb(4096, 14336, 32) > 0 and wb(4096, 14336, 32) % 256 == 0
+    assert wb(4096, 1024, 32) == 0         # too few pair steps to split
     assert wb(33, 320, 8) == 0
 
 

@@ -57,7 +57,8 @@ def _rows(N, count, seed):
 @pytest.mark.parametrize("M,N,K", [(32, 4096, 14336), (17, 4096, 14336), (24, 4096, 8192),
                                    (32, 1000, 8192), (20, 2000, 16384), (32, 37, 8320),
                                    (8, 4096, 14336), (32, 4096, 4096), (32, 6144, 4096),
-                                   (16, 1000, 2048)])
+                                   (16, 1000, 2048), (16, 4096, 14336), (5, 300, 8192),
+                                   (24, 5000, 2048), (32, 4100, 2048)])
 def test_split_matches_oracle_and_repeats(nf4, M, N, K):
     need = nf4.smallm_workspace_bytes(N, K, M)
     W = wl.weights(N, K, 0.02, seed=N + K + M, device=DEV)
@@ -85,7 +86,10 @@ def test_split_is_used_where_planned(nf4):
     assert nf4.smallm_workspace_bytes(4096, 14336, 32) > 0
     assert nf4.smallm_workspace_bytes(1000, 8192, 32) > 0
     assert nf4.smallm_workspace_bytes(37, 8320, 32) > 0
-    assert nf4.smallm_workspace_bytes(4096, 14336, 8) == 0
+    assert nf4.smallm_workspace_bytes(4096, 14336, 8) > 0
+    assert nf4.smallm_workspace_bytes(6144, 4096, 32) > 0
+    assert nf4.smallm_workspace_bytes(4096, 4096, 32) > 0
+    assert nf4.smallm_workspace_bytes(4096, 4096, 8) == 0
     assert nf4.smallm_workspace_bytes(28672, 4096, 32) == 0
 
 
@@ -125,3 +129,30 @@ def test_split_in_a_hip_graph(nf4):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(Y, ref), i
+
+
+def test_one_workspace_across_shapes_and_entry_points(nf4):
+    """One workspace, zero-filled once, serves split calls of different shapes and
+    both entry points in turn (the counter area has a fixed place and size, and
+    every call leaves it zero): each result equals a fresh-workspace call's bits."""
+    cases = [("smallm", 32, 4096, 14336), ("smallm", 32, 6144, 4096), ("smallm", 32, 4096, 4096),
+             ("prefill", 64, 4096, 14336), ("smallm", 8, 4096, 14336), ("prefill", 128, 2048, 4096),
+             ("smallm", 24, 5000, 2048), ("smallm", 32, 4096, 14336)]
+    need = max((nf4.smallm_workspace_bytes if e == "smallm" else nf4.prefill_workspace_bytes)(N, K, M)
+               for e, M, N, K in cases)
+    shared = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for i, (entry, M, N, K) in enumerate(cases):
+        fn = nf4.nf4_gemm_smallm_ws if entry == "smallm" else nf4.nf4_gemm_prefill_ws
+        wb = (nf4.smallm_workspace_bytes if entry == "smallm" else nf4.prefill_workspace_bytes)(N, K, M)
+        assert wb > 0, (entry, M, N, K)
+        W = wl.weights(N, K, 0.02, seed=500 + i, device=DEV)
+        X = wl.activations(M, K, seed=600 + i, device=DEV)
+        codes, scales = _pack(nf4, W)
+        Y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        fn(codes, scales, X, Y, shared)
+        fresh = torch.zeros(wb, dtype=torch.uint8, device=DEV)
+        Yf = torch.empty_like(Y)
+        fn(codes, scales, X, Yf, fresh)
+        torch.cuda.synchronize()
+        assert torch.equal(Y, Yf), f"{entry} M={M} N={N} K={K} on the shared workspace"
+        assert int(shared[:4096].count_nonzero().item()) == 0
