@@ -386,12 +386,17 @@ hipError_t go_prefill(const uint8_t *codes, const uint16_t *scales, int N, int K
 }
 
 // Workgroup tile (64 RM x 64 CN), in-workgroup K-splits KS and workgroup
-// K-splits S.  The tile is the largest of 128 x 128, 64 x 128, 64 x 64 that
-// still gives every CU a workgroup, else the smallest (128 x 64 is never needed:
-// 64 x 128 gives at least as many workgroups).  P (steps in flight, even: the
-// LDS stage alternates) and KS are as large as the registers allow.  With a
-// workspace, a grid of fewer than 256 workgroups is multiplied by the largest S
-// that keeps it within 256 (and at least two steps per wave).
+// K-splits S.  Larger tiles read each weight and activation byte for more
+// outputs, and pay even with fewer workgroups than CUs: a sweep of the tiles
+// and S on the Llama-3.1-8B shapes (M = 64 .. 512) picked 128 x 128 from M = 128
+// once the grid reaches about 180 workgroups (gate|up at M = 128: 134 -> 83 us;
+// q|k|v at M = 512, 192 workgroups: 101 -> 71 us), and for K >= 8192 at M >= 512
+// with workgroup K-splits filling the CUs (down at M = 512: 201 -> 141 us); then
+// 64 x 128 from M = 128 at about 180 workgroups (q|k|v at M = 256: 56 -> 47 us);
+// else 64 x 64 (at M = 64 it beats 64 x 128 even on 28672 rows).  P (steps in
+// flight, even: the LDS stage alternates) and KS are as large as the registers
+// allow.  With a workspace, a grid of fewer than 256 workgroups is multiplied by
+// the largest S that keeps it within 256 (and at least two steps per wave).
 struct PrefillPlan {
   int RM, CN, KS, S;
   int64_t tiles;
@@ -399,10 +404,11 @@ struct PrefillPlan {
 
 PrefillPlan plan_prefill(int n, int k, int m, bool split) {
   auto blocks = [&](int bm, int bn) { return (int64_t)cdiv(n, bn) * cdiv(m, bm); };
+  constexpr int kEnough = 180;  // workgroups for a large tile to pay
   PrefillPlan p;
-  if (blocks(128, 128) >= kCUs)
+  if (m >= 128 && (blocks(128, 128) >= kEnough || (m >= 512 && k >= 8192)))
     p = PrefillPlan{2, 2, 2, 1, blocks(128, 128)};
-  else if (blocks(64, 128) >= kCUs)
+  else if (m >= 128 && blocks(64, 128) >= kEnough)
     p = PrefillPlan{1, 2, 2, 1, blocks(64, 128)};
   else
     p = PrefillPlan{1, 1, 4, 1, blocks(64, 64)};
