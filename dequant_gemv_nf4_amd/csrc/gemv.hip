@@ -72,10 +72,12 @@ __global__ void __launch_bounds__(kThreads)
   // (13 argument words in all, so that every one arrives preloaded in scalar
   // registers: no argument load sits between a wave's start and its first loads)
   const int S = sgu & 15, G = (sgu >> 4) & 15, Us = sgu >> 8;
-  // rows of codes in flight per wave (registers).  Two for M = 1: measured
-  // deeper rings run slower, since a wave whose next load waits for room at the
-  // address unit cannot go on to compute rows whose data has arrived.
-  constexpr int kDepth = M > 1 ? 4 : 2;
+  // rows of codes in flight per wave (registers).  Two: measured deeper rings
+  // run slower at every M (three, four and six rows at M = 1; four and six at
+  // M = 2..4, e.g. 28672x4096 at M = 4 22.7 us with four, 20.9 with two), since
+  // a wave whose next load waits for room at the address unit cannot go on to
+  // compute rows whose data has arrived.
+  constexpr int kDepth = 2;
   // one LDS block carved by hand so that the decode table starts at offset 0: its
   // byte addresses (< 64 KiB) then need no base added before each read
   __shared__ __attribute__((aligned(16))) uint32_t lds[kLutWords + kRedFloats + kStageBytes / 4];

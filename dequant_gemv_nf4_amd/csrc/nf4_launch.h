@@ -17,14 +17,13 @@ hipError_t launch_gemv_valu(const uint8_t *codes, const uint16_t *scales, int64_
 bool valu_supported(int64_t N, int64_t K, int M);
 
 // Which kernel a batch of M rows runs on: the vector-ALU kernel (one weight
-// decode shared by M dot products) for M <= 2, for M = 3 on matrices of more
-// than 5120 rows and for M = 4 on more than 8192; the MFMA kernel otherwise.
-// Measured on the Llama-3.1-8B shapes (graph replays): MFMA wins from M = 5
-// everywhere, at M = 4 on 4096 rows (4096x4096: 6.3 vs 7.8 us) and at M = 3 on
-// 4096 rows (6.25 vs 7.05 us); VALU at M = 3 on 6144 rows (8.5 vs 9.2 us) and
-// 28672 rows (20.2 vs 27.5) and at M = 4 on 28672 rows (22.6 vs 27.8).
+// decode shared by M dot products) for M <= 2, and for M = 3 and 4 on matrices
+// of more than 5120 rows; the MFMA kernel otherwise.  Measured on the
+// Llama-3.1-8B shapes (graph replays): MFMA wins from M = 5 everywhere and at
+// M = 3 and 4 on 4096 rows (4096x4096 at M = 4: 6.5 vs 7.1 us); VALU at M = 3
+// and 4 on 6144 rows (M = 4: 8.2 vs 9.2 us) and 28672 rows (M = 4: 21.0 vs 27.9).
 inline bool use_valu(int64_t N, int64_t K, int M) {
-  return (M <= 2 || (M == 3 && N > 5120) || (M == 4 && N > 8192)) && valu_supported(N, K, M);
+  return (M <= 2 || (M <= 4 && N > 5120)) && valu_supported(N, K, M);
 }
 
 // Workspace layout of every K-splitting call (small-batch and prefill): the

@@ -35,8 +35,8 @@
  * memory is touched.  Asynchronous GPU faults surface on the stream as usual.
  *
  * Numerics: nf4_pack and nf4_unpack are exact (bit-for-bit defined below).
- * The products accumulate in fp32.  On the vector-ALU kernel (M <= 2, M = 3
- * on matrices of more than 5120 rows, M = 4 on more than 8192) the levels are f16 and each
+ * The products accumulate in fp32.  On the vector-ALU kernel (M <= 2, and
+ * M = 3 or 4 on matrices of more than 5120 rows) the levels are f16 and each
  * activation block is scaled by a power of two into f16; on the MFMA kernels
  * (every other M, and nf4_gemm_prefill) the levels are split into bf16 hi + lo
  * and the bf16 activations are used as they are.  Per output element
