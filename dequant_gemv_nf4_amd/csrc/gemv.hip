@@ -380,6 +380,10 @@ bool plan_valu(int64_t N, int64_t K, int M, Plan &p) {
   if (U > kMaxUnits || M * U * kUnitStageBytes > kStageBytes) return false;
   int S = 1;  // a power of two, so that S * G covers the 8 waves exactly
   while (S < cdiv(U, 64 * upl_cap(M))) S *= 2;
+  // where four units per lane fit a slice exactly, two units per lane in twice
+  // the slices (half the activation registers, the same lane use) ran faster:
+  // 8192x8192 9.5 -> 9.0 us, 57344x8192 42.4 -> 39.9 us
+  if (M == 1 && U == 256 * S && 2 * S <= kWaves) S *= 2;
   if (S > kWaves) return false;
   // widen the K split while there are too few rows to give every CU a row group
   while (2 * S <= kWaves && cdiv(N, std::max(1, kWaves / S)) < kCUs) S *= 2;
