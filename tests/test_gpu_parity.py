@@ -256,7 +256,10 @@ def test_full_size_layer_shapes_m1(nf4, set_):
         _full_size_case(nf4, set_, name, N, K, 1)
 
 
-@pytest.mark.parametrize("M", [4, 8, 32])
+# M = 2, 3, 4: the vector-ALU kernel on the wide matrices and the MFMA kernel on the
+# 4096-row ones (both sides of the dispatch threshold); 8, 16, 32: the MFMA kernel
+# with its K-split plans (through gemm(), which brings a workspace)
+@pytest.mark.parametrize("M", [2, 3, 4, 8, 16, 32])
 def test_full_size_smallm_8b(nf4, M):
     for name, N, K in _launch_shapes(wl.SET_8B_SMALLM):
         _full_size_case(nf4, wl.SET_8B_SMALLM, name, N, K, M)
