@@ -30,8 +30,10 @@ __device__ __forceinline__ uint32_t bf16_of_exact(float p, float e) {
   return r + (up ? 1u : 0u);
 }
 
-__device__ __forceinline__ uint32_t embed_pair(uint32_t byte, float s) {
-  const float l0 = level_f32(byte & 15u), l1 = level_f32(byte >> 4);
+// levels from a 16-entry table in LDS: the entries sit in 16 distinct banks, so
+// lanes reading different levels never conflict and equal ones broadcast
+__device__ __forceinline__ uint32_t embed_pair(const float *lv, uint32_t byte, float s) {
+  const float l0 = lv[byte & 15u], l1 = lv[byte >> 4];
   const float p0 = __fmul_rn(l0, s), p1 = __fmul_rn(l1, s);
   const float e0 = __fmaf_rn(l0, s, -p0), e1 = __fmaf_rn(l1, s, -p1);
   return bf16_of_exact(p0, e0) | (bf16_of_exact(p1, e1) << 16);
@@ -39,27 +41,45 @@ __device__ __forceinline__ uint32_t embed_pair(uint32_t byte, float s) {
 
 constexpr int kEmbedThreads = 256;
 
+// One thread decodes chunk c (8 values) of RPT consecutive rows; the rows' loads
+// are all issued before any is used, so a wave has RPT code words in flight
+// instead of one.  Block b covers chunk block b % bpr of row group b / bpr.
+template <int RPT>
 __global__ void __launch_bounds__(kEmbedThreads)
     embed_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, int N,
-                 int K, const int64_t *__restrict__ ids, uint16_t *__restrict__ out,
+                 int K, const int64_t *__restrict__ ids, int64_t T, uint16_t *__restrict__ out,
                  int32_t *status, int blocks_per_row) {
-  const int t = blockIdx.x / blocks_per_row;
-  const int c = (blockIdx.x - t * blocks_per_row) * kEmbedThreads + threadIdx.x;  // 8-value chunk
+  __shared__ float lv[16];
+  if (threadIdx.x < 16) lv[threadIdx.x] = level_f32(threadIdx.x);
+  __syncthreads();
+  const int g = blockIdx.x / blocks_per_row;
+  const int c = (blockIdx.x - g * blocks_per_row) * kEmbedThreads + threadIdx.x;  // 8-value chunk
   if (c >= (K >> 3)) return;
-  const int64_t id = ids[t];
-  uint4 o = make_uint4(0u, 0u, 0u, 0u);
-  if (id < 0 || id >= N) {
-    if (c == 0 && status) atomicOr(status, 1);
-  } else {
-    const uint32_t w =
-        *reinterpret_cast<const uint32_t *>(codes + id * (int64_t)(K >> 1) + (int64_t)c * 4);
-    const float s = f16_bits_to_f32(scales[id * (int64_t)(K >> 6) + (c >> 3)]);
-    o.x = embed_pair(w & 0xFFu, s);
-    o.y = embed_pair((w >> 8) & 0xFFu, s);
-    o.z = embed_pair((w >> 16) & 0xFFu, s);
-    o.w = embed_pair(w >> 24, s);
+  const int64_t t0 = (int64_t)g * RPT;
+  uint32_t w[RPT];
+  float s[RPT];
+  bool ok[RPT];
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int64_t id = t0 + j < T ? ids[t0 + j] : 0;
+    ok[j] = id >= 0 && id < N;
+    if (!ok[j] && t0 + j < T && c == 0 && status) atomicOr(status, 1);
+    const int64_t r = ok[j] ? id : 0;  // a bad id reads row 0 and writes zeros
+    w[j] = *reinterpret_cast<const uint32_t *>(codes + r * (int64_t)(K >> 1) + (int64_t)c * 4);
+    s[j] = f16_bits_to_f32(scales[r * (int64_t)(K >> 6) + (c >> 3)]);
   }
-  *reinterpret_cast<uint4 *>(out + (int64_t)t * K + (int64_t)c * 8) = o;
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    if (t0 + j >= T) break;
+    uint4 o = make_uint4(0u, 0u, 0u, 0u);
+    if (ok[j]) {
+      o.x = embed_pair(lv, w[j] & 0xFFu, s[j]);
+      o.y = embed_pair(lv, (w[j] >> 8) & 0xFFu, s[j]);
+      o.z = embed_pair(lv, (w[j] >> 16) & 0xFFu, s[j]);
+      o.w = embed_pair(lv, w[j] >> 24, s[j]);
+    }
+    *reinterpret_cast<uint4 *>(out + (t0 + j) * K + (int64_t)c * 8) = o;
+  }
 }
 
 __global__ void clear_embed_status_kernel(int32_t *status) { *status = 0; }
@@ -75,8 +95,23 @@ hipError_t launch_embed(const uint8_t *codes, const uint16_t *scales, int64_t N,
   if (T == 0) return hipSuccess;
   const int chunks = (int)(K >> 3);
   const int bpr = (chunks + kEmbedThreads - 1) / kEmbedThreads;
-  hipLaunchKernelGGL(embed_kernel, dim3((unsigned)(T * bpr)), dim3(kEmbedThreads), 0, stream,
-                     codes, scales, (int)N, (int)K, ids, out, status, bpr);
+  // rows per thread: keep about two waves' worth of blocks per SIMD before
+  // trading blocks for loads in flight
+  const int64_t blocks1 = T * bpr;
+  const int rpt = blocks1 >= 8 * 2048 ? 8 : blocks1 >= 4 * 2048 ? 4 : blocks1 >= 2 * 2048 ? 2 : 1;
+  const unsigned grid = (unsigned)(((T + rpt - 1) / rpt) * bpr);
+  if (rpt == 8)
+    hipLaunchKernelGGL(embed_kernel<8>, dim3(grid), dim3(kEmbedThreads), 0, stream, codes,
+                       scales, (int)N, (int)K, ids, T, out, status, bpr);
+  else if (rpt == 4)
+    hipLaunchKernelGGL(embed_kernel<4>, dim3(grid), dim3(kEmbedThreads), 0, stream, codes,
+                       scales, (int)N, (int)K, ids, T, out, status, bpr);
+  else if (rpt == 2)
+    hipLaunchKernelGGL(embed_kernel<2>, dim3(grid), dim3(kEmbedThreads), 0, stream, codes,
+                       scales, (int)N, (int)K, ids, T, out, status, bpr);
+  else
+    hipLaunchKernelGGL(embed_kernel<1>, dim3(grid), dim3(kEmbedThreads), 0, stream, codes,
+                       scales, (int)N, (int)K, ids, T, out, status, bpr);
   return hipGetLastError();
 }
 

@@ -105,3 +105,19 @@ def test_embed_llama_vocab_rows(nf4):
     assert np.array_equal(codes[torch.from_numpy(rows).to(DEV)].cpu().numpy(), ref_p)
     want, _ = oracle.embed(ref_p, ref_s, np.searchsorted(rows, ids))
     assert np.array_equal(_bits(out), want)
+
+
+@pytest.mark.parametrize("T,K", [(2049, 4096), (4099, 2112), (8195, 1024), (16387, 1024)])
+def test_embed_many_rows_ragged(nf4, T, K):
+    """Enough ids that a thread decodes several rows (the row count is not a
+    multiple of that), a ragged chunk block when K/8 is not a multiple of 256,
+    and bad ids in the first, a middle and the last row."""
+    rng = np.random.default_rng(T + K)
+    W = (rng.standard_normal((64, K)) * 0.02).astype(np.float32)
+    p, s, _ = oracle.quantize_pack(W)
+    ids = rng.integers(0, 64, T).astype(np.int64)
+    ids[0], ids[T // 2], ids[-1] = -3, 64, 1 << 33
+    got, st = _run(nf4, p, s, ids)
+    want, wst = oracle.embed(p, s, ids)
+    assert st == wst == oracle.EMBED_BAD_ID
+    assert np.array_equal(got, want)
