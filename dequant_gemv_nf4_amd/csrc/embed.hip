@@ -6,8 +6,9 @@
 // the exact product: p = the fp32 product, e = its exact error (one fma); p
 // decides the bf16 rounding except on an exact bf16 tie, where the sign of e
 // says on which side of it the exact product lies.  One thread writes 8
-// outputs (one 32-bit word of codes, 16 bytes of output).  An id outside
-// [0, N) gives a zero row and sets bit NF4_EMBED_BAD_ID of the status word.
+// outputs of a row (one 32-bit word of codes, 16 bytes of output), in 1, 2, 4
+// or 8 consecutive rows.  An id outside [0, N) gives a zero row and sets bit
+// NF4_EMBED_BAD_ID of the status word.
 #include "nf4_device.h"
 #include "nf4_launch.h"
 

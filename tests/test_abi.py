@@ -130,7 +130,9 @@ def test_smallm_workspace_sizes(lib):
     assert wb(4096, 14336, 4) == 0         # M = 4 on the matrix cores: neither
     assert wb(4096, 4096, 32) > 0          # one tile per CU at M > 16: two splits
     assert wb(6144, 4096, 32) > 0          # fewer workgroups than CUs: three tiles, two splits
-    assert wb(4096, 14336, 8) > 0          # long K from M = 5: two tiles, two splits
+    assert wb(4096, 14336, 16) > 0         # long K at M 5..16: two tiles, two splits
+    assert wb(4096, 14336, 8) == 0         # ...except M <= 8 with K % 256 == 0 (quad steps)
+    assert wb(4096, 14464, 8) > 0          # (K = 14464: 226 groups, pair steps, split)
     assert wb(4096, 14336, 32) > 0 and wb(4096, 14336, 32) % 256 == 0
     assert wb(4096, 1024, 32) == 0         # too few pair steps to split
     assert wb(33, 320, 8) == 0

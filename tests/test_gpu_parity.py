@@ -165,6 +165,35 @@ def test_gemm_smallm_shapes(nf4, M, N, K):
     _product_case(nf4, M, N, K, seed=3)
 
 
+@pytest.mark.parametrize("M,N,K", [(3, 300, 256), (4, 1, 256), (8, 8, 1024), (8, 300, 512),
+                                   (6, 4097, 1024), (5, 4111, 3328), (7, 12304, 2048),
+                                   (8, 28688, 768)])
+def test_gemm_quad_steps(nf4, M, N, K):
+    """M <= 8 with K a multiple of 256 runs four groups per step: one step per
+    row (K = 256: seven of the eight waves idle), step counts the eight waves do
+    not share evenly (K = 768, 3328), fewer rows than a tile, rows past N in the
+    last tile, and 2, 4 column tiles per workgroup with a ragged last group."""
+    _product_case(nf4, M, N, K, seed=4)
+
+
+def test_gemm_quad_shape_with_scales_only_4_byte_aligned(nf4):
+    """Scales 4 but not 8 bytes aligned: the quad-step shape falls back to the
+    pair-step kernel, without a K-split (no workspace is planned for it)."""
+    M, N, K = 8, 96, 14336
+    assert nf4.smallm_workspace_bytes(N, K, M) == 0
+    W = wl.weights(N, K, 0.02, seed=61, device=DEV)
+    codes, scales = _pack_gpu(nf4, W)[:2]
+    buf = torch.zeros(N * (K // 64) + 2, dtype=torch.int16, device=DEV)
+    buf[2:].copy_(scales.view(-1))
+    sc = buf[2:].view(N, K // 64)
+    assert sc.data_ptr() % 8 == 4
+    X = wl.activations(M, K, seed=71, device=DEV)
+    Y = nf4.gemm(codes, sc, X)
+    torch.cuda.synchronize()
+    Yr, A = oracle.gemm(codes.cpu().numpy(), _u16(scales), wl.bf16_bits(X))
+    _check_product(Y.reshape(M, N), Yr, A, "scales 4-byte aligned, M=8")
+
+
 def test_product_exact_identities(nf4):
     N, K = 300, 1024
     W = wl.weights(N, K, 0.02, seed=5, device=DEV)

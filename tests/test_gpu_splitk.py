@@ -86,7 +86,8 @@ def test_split_is_used_where_planned(nf4):
     assert nf4.smallm_workspace_bytes(4096, 14336, 32) > 0
     assert nf4.smallm_workspace_bytes(1000, 8192, 32) > 0
     assert nf4.smallm_workspace_bytes(37, 8320, 32) > 0
-    assert nf4.smallm_workspace_bytes(4096, 14336, 8) > 0
+    assert nf4.smallm_workspace_bytes(4096, 14336, 16) > 0
+    assert nf4.smallm_workspace_bytes(4096, 14336, 8) == 0  # quad steps: no split
     assert nf4.smallm_workspace_bytes(6144, 4096, 32) > 0
     assert nf4.smallm_workspace_bytes(4096, 4096, 32) > 0
     assert nf4.smallm_workspace_bytes(4096, 4096, 8) == 0
@@ -136,7 +137,7 @@ def test_one_workspace_across_shapes_and_entry_points(nf4):
     both entry points in turn (the counter area has a fixed place and size, and
     every call leaves it zero): each result equals a fresh-workspace call's bits."""
     cases = [("smallm", 32, 4096, 14336), ("smallm", 32, 6144, 4096), ("smallm", 32, 4096, 4096),
-             ("prefill", 64, 4096, 14336), ("smallm", 8, 4096, 14336), ("prefill", 128, 2048, 4096),
+             ("prefill", 64, 4096, 14336), ("smallm", 16, 4096, 14336), ("prefill", 128, 2048, 4096),
              ("smallm", 24, 5000, 2048), ("smallm", 32, 4096, 14336)]
     need = max((nf4.smallm_workspace_bytes if e == "smallm" else nf4.prefill_workspace_bytes)(N, K, M)
                for e, M, N, K in cases)
