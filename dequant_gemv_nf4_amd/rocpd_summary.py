@@ -1,12 +1,14 @@
 """Summaries of rocprofv3 result databases (rocpd SQLite) for the NF4 kernels.
 
-    python -m dequant_gemv_nf4_amd.rocpd_summary trace  <results.db> [name-filter]
-    python -m dequant_gemv_nf4_amd.rocpd_summary pmc    <results.db> [name-filter]
+    python -m dequant_gemv_nf4_amd.rocpd_summary trace  <results.db> [name-filter] [prev]
+    python -m dequant_gemv_nf4_amd.rocpd_summary pmc    <results.db> [name-filter] [prev]
     python -m dequant_gemv_nf4_amd.rocpd_summary copies <results.db> [name-filter]
 
 `trace` groups dispatches by (kernel, grid, workgroup) and prints count, mean,
 median, p10 and p90 duration.  `pmc` prints the mean of every collected counter
-per (kernel, grid).  `copies` groups memory copies by direction and size (count,
+per (kernel, grid).  With the word `prev`, each group is split further by the
+kernel dispatched just before (labelled "after <kernel>"): two shapes that
+share a kernel and a grid but follow different launches come apart.  `copies` groups memory copies by direction and size (count,
 mean duration, GB/s), then reports how the copies and the filtered kernels
 overlap in time: the busy time of the copy engine over the span from the first
 to the last copy, and how many kernels ran while a copy was in flight.  All
@@ -22,14 +24,17 @@ def _short(name: str) -> str:
     return name.split("(")[0].replace("void ", "")
 
 
-def trace(path, filt=""):
+def trace(path, filt="", by_prev=False):
     db = sqlite3.connect(path)
     rows = db.execute("select name, grid_x, workgroup_x, start, end from kernels order by start")
     groups = collections.OrderedDict()
+    prev = "-"
     for name, gx, wx, s, e in rows:
+        short, before, prev = _short(name), prev, _short(name)
         if filt and filt not in name:
             continue
-        groups.setdefault((_short(name), gx, wx), []).append((e - s) / 1e3)
+        key = (short + (f" after {before}" if by_prev else ""), gx, wx)
+        groups.setdefault(key, []).append((e - s) / 1e3)
     out = []
     for (name, gx, wx), d in groups.items():
         d = sorted(d)
@@ -39,18 +44,25 @@ def trace(path, filt=""):
     return out
 
 
-def pmc(path, filt=""):
+def pmc(path, filt="", by_prev=False):
     db = sqlite3.connect(path)
-    rows = db.execute("select kernel_name, grid_size, counter_name, value from counters_collection")
-    agg = collections.OrderedDict()
-    for name, grid, counter, value in rows:
-        if filt and filt not in name:
+    rows = db.execute("select dispatch_id, kernel_name, grid_size, counter_name, value "
+                      "from counters_collection order by dispatch_id")
+    disp = collections.OrderedDict()  # dispatch -> (kernel, grid, {counter: value})
+    for did, name, grid, counter, value in rows:
+        disp.setdefault(did, (_short(name), grid, collections.defaultdict(float)))[2][counter] += value
+    groups = collections.OrderedDict()
+    prev = "-"
+    for short, grid, vals in disp.values():
+        before, prev = prev, short
+        if filt and filt not in short:
             continue
-        agg.setdefault((_short(name), grid), collections.defaultdict(list))[counter].append(value)
+        key = (short + (f" after {before}" if by_prev else ""), grid)
+        groups.setdefault(key, []).append(vals)
     out = []
-    for (name, grid), d in agg.items():
-        vals = ", ".join(f"{k}={statistics.mean(v):.1f}" for k, v in sorted(d.items()))
-        out.append(f"{name:48s} grid {grid:8d} n {len(next(iter(d.values()))):4d}  {vals}")
+    for (name, grid), ds in groups.items():
+        vals = ", ".join(f"{c}={statistics.mean(d[c] for d in ds):.1f}" for c in sorted(ds[0]))
+        out.append(f"{name:48s} grid {grid:8d} n {len(ds):4d}  {vals}")
     return out
 
 
@@ -91,5 +103,8 @@ def copies(path, filt=""):
 if __name__ == "__main__":
     mode, path = sys.argv[1], sys.argv[2]
     filt = sys.argv[3] if len(sys.argv) > 3 else ""
-    fn = {"trace": trace, "pmc": pmc, "copies": copies}[mode]
-    print("\n".join(fn(path, filt)))
+    if mode == "copies":
+        print("\n".join(copies(path, filt)))
+    else:
+        by_prev = len(sys.argv) > 4 and sys.argv[4] == "prev"
+        print("\n".join({"trace": trace, "pmc": pmc}[mode](path, filt, by_prev)))
