@@ -110,8 +110,8 @@ int nf4_gemv(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
  * nf4_gemm_smallm -- Y[m][n] = sum_k L[code(n,k)] * s(n,k/64) * X[m][k] for
  * 1 <= M <= 32 (prefill chunks, speculative verification batches).
  * Source: deep-fold README, "Method" (prompt chunks of up to 32 positions on a
- * tensor-core NF4 GEMM).  M = 1 is the GEMV; from M = 5 (M = 4 on matrices of
- * up to 8192 rows) the product runs on MFMA.
+ * tensor-core NF4 GEMM).  M = 1 is the GEMV; from M = 5 (M = 3 and 4 on
+ * matrices of up to 5120 rows) the product runs on MFMA.
  * Alignment: codes 16 bytes, scales 2, X 16, Y 4.
  */
 int nf4_gemm_smallm(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
