@@ -489,8 +489,9 @@ __global__ void __launch_bounds__(kThreads)
 // outputs are never stored.)
 //
 // Work: wave w of the workgroup takes a contiguous range of the steps; no
-// K-splits.  Measured on the Llama-3.1-8B shapes at M = 8 against the pair
-// step: gate|up 28672 x 4096 32.3 -> 25.7 us, down 4096 x 14336 16.4 -> 14.8.
+// K-splits.  Kernel trace of the Llama-3.1-8B shapes at M = 8 (graph replay),
+// pair step -> quad step: q|k|v 6144 x 4096 10.5 -> 9.8 us, o 4096 x 4096
+// 7.6 -> 7.4, gate|up 28672 x 4096 29.6 -> 27.2, down 4096 x 14336 16.8 -> 15.2.
 // ---------------------------------------------------------------------------
 template <int TB>
 __global__ void __launch_bounds__(kThreads)
