@@ -266,6 +266,39 @@ def _full_size_case(nf4, set_, proj, N, K, M):
     del W
 
 
+@pytest.mark.parametrize("set_", [wl.SET_7B, wl.SET_13B, wl.SET_70B, wl.SET_8B_SMALLM],
+                         ids=lambda s: s.name)
+def test_pack_first_middle_last_layers(nf4, set_):
+    """Packing of layers 0, L/2 and L-1 of the set, each with its own seeds: 64
+    random rows of every projection, plus the first and last row, bit-exact
+    against the oracle's quantizer."""
+    for layer in (0, set_.layers // 2, set_.layers - 1):
+        for proj, N, K in set_.projections:
+            W = wl.weights(N, K, set_.sigma, wl.seed_for(set_.name, layer, proj, "W"), device=DEV)
+            codes, scales, st = _pack_gpu(nf4, W)
+            assert st == 0
+            r = torch.from_numpy(_sampled_rows(N, 64, 7919 * layer + N + K)).to(DEV)
+            ref_p, ref_s, _ = oracle.quantize_pack(W[r].cpu().numpy())
+            what = f"{set_.name} layer {layer} {proj}"
+            assert np.array_equal(codes[r].cpu().numpy(), ref_p), what + " codes"
+            assert np.array_equal(_u16(scales[r]), ref_s), what + " scales"
+            del W, codes, scales
+
+
+def test_pack_whole_matrices_of_a_7b_layer(nf4):
+    """Every row of every projection of the 7B set's middle layer, bit-exact."""
+    layer = wl.SET_7B.layers // 2
+    for proj, N, K in wl.SET_7B.projections:
+        W = wl.weights(N, K, wl.SET_7B.sigma, wl.seed_for(wl.SET_7B.name, layer, proj, "W"),
+                       device=DEV)
+        codes, scales, st = _pack_gpu(nf4, W)
+        assert st == 0
+        ref_p, ref_s, _ = oracle.quantize_pack(W.cpu().numpy())
+        assert np.array_equal(codes.cpu().numpy(), ref_p), f"7B layer {layer} {proj} codes"
+        assert np.array_equal(_u16(scales), ref_s), f"7B layer {layer} {proj} scales"
+        del W, codes, scales
+
+
 def _launch_shapes(set_):
     """(name, N, K) of every distinct product shape of a layer, one launch per
     projection and with same-x projections fused along N."""
