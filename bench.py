@@ -84,6 +84,20 @@ def recorded_traffic(key):
     return None
 
 
+def kernel_label(M, N, K):
+    """Name of the kernel a product of this shape runs, by the library's dispatch
+    rule (a label for the bench line only): the vector-ALU GEMV for M <= 2 and for
+    M = 3, 4 above 5120 rows; MFMA quad steps for M <= 8 when K is a multiple of
+    256; MFMA pair steps up to M = 32; the prefill tiles beyond."""
+    if M <= 2 or (M <= 4 and N > 5120):
+        return "gemv_valu_kernel"
+    if M <= 8 and K % 256 == 0:
+        return "gemm_mfma_quad_kernel"
+    if M <= 32:
+        return "gemm_mfma_pair_kernel" if (K // 64) % 2 == 0 else "gemm_mfma_kernel"
+    return "gemm_prefill_kernel"
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -496,8 +510,8 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    kname = ("gemv_valu_kernel" if M < 8 else "gemm_mfma_kernel" if M <= nf4.MAX_M
-             else "gemm_prefill_kernel")
+    kname = " + ".join(sorted({kernel_label(M, per_proj[p]["N"], per_proj[p]["K"])
+                               for p in dom["projs"]}))
     roof.update({"traffic": recorded_traffic(f"M={M} {set_.name} " + ",".join(dom["projs"])),
                  "kernel": f"{kname} (M={M}, K={dom_k})", "projections": dom["projs"],
                  "bytes_per_launch": float(np.mean(dom["launch_bytes"])),

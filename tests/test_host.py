@@ -90,3 +90,16 @@ def test_cpu_baseline_leg_reports_the_contract_keys():
     assert set(out) >= {"value", "unit", "cores", "kind", "sample"}
     assert out["kind"] == "oracle" and out["cores"] == 1 and out["value"] > 0
     assert np.isfinite(out["value"])
+
+
+@pytest.mark.parametrize("M,N,K,name", [
+    (1, 4096, 4096, "gemv_valu_kernel"), (2, 28672, 4096, "gemv_valu_kernel"),
+    (4, 6144, 4096, "gemv_valu_kernel"), (4, 4096, 4096, "gemm_mfma_quad_kernel"),
+    (3, 4096, 14336, "gemm_mfma_quad_kernel"), (8, 28672, 4096, "gemm_mfma_quad_kernel"),
+    (8, 4096, 14464, "gemm_mfma_pair_kernel"), (16, 4096, 4096, "gemm_mfma_pair_kernel"),
+    (32, 100, 320, "gemm_mfma_kernel"), (64, 4096, 4096, "gemm_prefill_kernel")])
+def test_bench_kernel_label(M, N, K, name):
+    """The bench line names the kernel the dispatch rule picks (vector ALU for
+    M <= 2 and M = 3, 4 above 5120 rows; quad steps for M <= 8 and K % 256 == 0;
+    pair steps for an even group count up to M = 32; prefill beyond)."""
+    assert bench.kernel_label(M, N, K) == name
