@@ -103,3 +103,31 @@ def test_bench_kernel_label(M, N, K, name):
     M <= 2 and M = 3, 4 above 5120 rows; quad steps for M <= 8 and K % 256 == 0;
     pair steps for an even group count up to M = 32; prefill beyond)."""
     assert bench.kernel_label(M, N, K) == name
+
+
+def test_rocpd_summary_splits_by_preceding_kernel(tmp_path):
+    """Two shapes that share a kernel and a grid (o after q|k|v, down after
+    gate|up) come apart when groups are keyed by the kernel dispatched before."""
+    import sqlite3
+    from dequant_gemv_nf4_amd import rocpd_summary as rs
+    db = sqlite3.connect(tmp_path / "r.db")
+    db.execute("create table kernels (name text, grid_x int, workgroup_x int, start int, end int)")
+    db.execute("create table counters_collection (dispatch_id int, kernel_name text, "
+               "grid_size int, counter_name text, value real)")
+    seq = [("A(int)", 1, 10), ("B(int)", 2, 3), ("C(int)", 3, 30), ("B(int)", 2, 5)] * 3
+    t = 0
+    for i, (name, grid, dur_us) in enumerate(seq):
+        db.execute("insert into kernels values (?, ?, 64, ?, ?)", (name, grid, t, t + dur_us * 1000))
+        db.execute("insert into counters_collection values (?, ?, ?, 'X', ?)", (i, name, grid, dur_us))
+        t += dur_us * 1000 + 500
+    db.commit()
+    plain = rs.trace(str(tmp_path / "r.db"), "B")
+    assert len(plain) == 1 and " n     6 " in plain[0]
+    split = rs.trace(str(tmp_path / "r.db"), "B", True)
+    assert len(split) == 2
+    after_a = next(l for l in split if "after A" in l)
+    after_c = next(l for l in split if "after C" in l)
+    assert "mean     3.000" in after_a and "mean     5.000" in after_c
+    pm = rs.pmc(str(tmp_path / "r.db"), "B", True)
+    assert any("after A" in l and "X=3.0" in l for l in pm)
+    assert any("after C" in l and "X=5.0" in l for l in pm)
