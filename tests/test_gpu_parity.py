@@ -166,6 +166,7 @@ def test_gemm_smallm_shapes(nf4, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(3, 300, 256), (4, 1, 256), (8, 8, 1024), (8, 300, 512),
+                                   (4, 4111, 3328), (3, 8, 1024), (4, 5120, 1024),
                                    (6, 4097, 1024), (5, 4111, 3328), (7, 12304, 2048),
                                    (8, 28688, 768)])
 def test_gemm_quad_steps(nf4, M, N, K):
