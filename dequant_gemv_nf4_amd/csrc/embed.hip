@@ -7,8 +7,10 @@
 // decides the bf16 rounding except on an exact bf16 tie, where the sign of e
 // says on which side of it the exact product lies.  One thread writes 8
 // outputs of a row (one 32-bit word of codes, 16 bytes of output), in 1, 2, 4
-// or 8 consecutive rows.  An id outside [0, N) gives a zero row and sets bit
-// NF4_EMBED_BAD_ID of the status word.
+// or 8 consecutive rows.  The rows are written with non-temporal stores (they
+// are 80 % of the bytes and are not read back here; T = 32768: 78 -> 65 us).
+// An id outside [0, N) gives a zero row and sets bit NF4_EMBED_BAD_ID of the
+// status word.
 #include "nf4_device.h"
 #include "nf4_launch.h"
 
@@ -79,7 +81,9 @@ __global__ void __launch_bounds__(kEmbedThreads)
       o.z = embed_pair(lv, (w[j] >> 16) & 0xFFu, s[j]);
       o.w = embed_pair(lv, w[j] >> 24, s[j]);
     }
-    *reinterpret_cast<uint4 *>(out + (t0 + j) * K + (int64_t)c * 8) = o;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(u32x4{o.x, o.y, o.z, o.w},
+                                reinterpret_cast<u32x4 *>(out + (t0 + j) * K + (int64_t)c * 8));
   }
 }
 
