@@ -61,6 +61,7 @@ constexpr int kRedFloats = 4096;                        // cross-slice partials 
 constexpr int kStageBytes = 163840 - 4 * kLutWords - 4 * kRedFloats;  // 80 KiB for activations
 constexpr int kUnitStageBytes = 64 + 4;                 // 32 f16 + a shift, per (row, unit)
 constexpr int kMaxUnits = 1024;                         // K <= 32768
+constexpr int kWideUnit = 0x40000000;  // staged shift of a unit that f16 cannot hold exactly
 // activation chunks (16 bytes) per thread: all of M * K fits the stage in one go
 constexpr int kXChunks = (kStageBytes / kUnitStageBytes * 4 + kThreads - 1) / kThreads;
 
@@ -216,18 +217,26 @@ __global__ void __launch_bounds__(kThreads)
       const uint4 v = xr[j];
       uint32_t mx = max(max(bf16x2_absmax_bits(v.x), bf16x2_absmax_bits(v.y)),
                         max(bf16x2_absmax_bits(v.z), bf16x2_absmax_bits(v.w)));
+      uint32_t mn = min(min(bf16x2_absmin_nz_bits(v.x), bf16x2_absmin_nz_bits(v.y)),
+                        min(bf16x2_absmin_nz_bits(v.z), bf16x2_absmin_nz_bits(v.w)));
       mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0xB1, 0xf, 0xf, false));
       mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x4E, 0xf, 0xf, false));
+      mn = min(mn, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mn, 0xB1, 0xf, 0xf, false));
+      mn = min(mn, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mn, 0x4E, 0xf, 0xf, false));
       if (c < nchunks) {  // nchunks is a multiple of 4: a quad is valid or not as a whole
         const int sh = f16_range_shift(mx);
+        const bool wide = f16_unit_inexact(mx, mn);
         const int q = c & 3;
         const int mu = c >> 2;  // m * U + u
         const int m = mu / U;
         const int u = mu - m * U;
+        // a unit f16 cannot hold exactly is staged as zeros: the row loop adds
+        // nothing for it, and the exact pass after the loop adds its terms
         stage_x[(q * M + m) * U + u] =
-            make_uint4(bf16x2_to_f16x2(v.x, sh), bf16x2_to_f16x2(v.y, sh),
-                       bf16x2_to_f16x2(v.z, sh), bf16x2_to_f16x2(v.w, sh));
-        if (q == 0) stage_sh[mu] = sh;
+            wide ? make_uint4(0u, 0u, 0u, 0u)
+                 : make_uint4(bf16x2_to_f16x2(v.x, sh), bf16x2_to_f16x2(v.y, sh),
+                              bf16x2_to_f16x2(v.z, sh), bf16x2_to_f16x2(v.w, sh));
+        if (q == 0) stage_sh[mu] = wide ? kWideUnit : sh;
       }
     }
   }
@@ -237,6 +246,7 @@ __global__ void __launch_bounds__(kThreads)
   // with a load in flight, and wait for it)
   const int rows_stride = __builtin_amdgcn_readfirstlane(U);
   const int q_stride = __builtin_amdgcn_readfirstlane(M * U);
+  uint32_t wide_bits = 0;  // bit m * UPL + i: unit i of activation row m is wide
 #pragma unroll
   for (int m = 0; m < M; ++m)
 #pragma unroll
@@ -251,7 +261,9 @@ __global__ void __launch_bounds__(kThreads)
           xh[m][i][4 * q + 2] = t.z;
           xh[m][i][4 * q + 3] = t.w;
         }
-        xf[m][i] = ldexpf(1.0f, -stage_sh[m * rows_stride + unit[i]]);
+        const int sh = stage_sh[m * rows_stride + unit[i]];
+        if (sh == kWideUnit) wide_bits |= 1u << (m * UPL + i);
+        xf[m][i] = sh == kWideUnit ? 0.0f : ldexpf(1.0f, -sh);
       } else {
 #pragma unroll
         for (int q = 0; q < 16; ++q) xh[m][i][q] = 0;
@@ -346,6 +358,61 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
   for (int d = 0; d < kDepth - 1; ++d)
     if (it + d < iters) compute_row(row0 + grp + (it + d) * rstride, it + d, cb[d], sb[d]);
+
+  // ---- exact pass, only in waves holding a unit that f16 cannot hold exactly
+  // (its activations span more than 2^28 in exponent; about 1e-8 of the units
+  // of N(0, 1) data).  The row loop added nothing for such a unit; here each of
+  // its weights is computed as (f16 level x fp32 group scale), exact, times the
+  // bf16 activation with one fp32 fma, so every term is w~ * x rounded once and
+  // no partial sum is formed before the scale is applied.  The wave's row sums
+  // are then added to the row partials it left in LDS.
+  if (__builtin_amdgcn_ballot_w64(wide_bits != 0) != 0) {
+    for (int t = 0; t < iters; ++t) {
+      const int r = row0 + grp + t * rstride;
+      if (r >= N) break;  // uniform: rows grow with t
+      float acc[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < UPL; ++i) {
+        uint32_t mine = 0;
+#pragma unroll
+        for (int m = 0; m < M; ++m) mine |= wide_bits & (1u << (m * UPL + i));
+        if (mine) {
+          const uint4 c = *reinterpret_cast<const uint4 *>(codes + (int64_t)r * row_bytes +
+                                                           16 * unit[i]);
+          const float sc = f16_bits_to_f32(scales[(int64_t)r * row_groups + (unit[i] >> 1)]);
+          const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            uint32_t lv[4];
+            lv[0] = lds_load_u32(lut, lut_addr<0>(cw[j], laneoff));
+            lv[1] = lds_load_u32(lut, lut_addr<1>(cw[j], laneoff));
+            lv[2] = lds_load_u32(lut, lut_addr<2>(cw[j], laneoff));
+            lv[3] = lds_load_u32(lut, lut_addr<3>(cw[j], laneoff));
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+              if (wide_bits & (1u << (m * UPL + i))) {
+                const uint32_t *xw =
+                    reinterpret_cast<const uint32_t *>(X + (int64_t)m * K + 32 * unit[i]) + 4 * j;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                  const uint32_t x2 = xw[b];
+                  acc[m] = fmaf(f16_bits_to_f32(lv[b] & 0xffffu) * sc, bf16_lo(x2), acc[m]);
+                  acc[m] = fmaf(f16_bits_to_f32(lv[b] >> 16) * sc, bf16_hi(x2), acc[m]);
+                }
+              }
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const float tsum = wave_sum(acc[m]);
+        if (lane == 0) red[(m * rows_per_block + t * G + grp) * S + slice] += tsum;
+      }
+    }
+  }
   {
     __syncthreads();
     for (int t = tid; t < M * rows_per_block; t += kThreads) {

@@ -24,8 +24,10 @@
  *
  * Ownership and execution:
  *  - Every array argument is a device pointer owned by the caller.  The library
- *    never frees or keeps a pointer, never writes its inputs, and keeps no
- *    per-call state, so calls on different streams may run concurrently.
+ *    never frees or keeps a pointer and never writes its inputs.  The only
+ *    state it keeps between calls is a per-device cache of "is this device
+ *    gfx950" (filled on a device's first call, read-only afterwards), so calls
+ *    on different streams may run concurrently.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
  *    call only enqueues work on it and returns; there is no synchronization.
  *  - Outputs are fully overwritten (no accumulation into y / Y).
@@ -37,12 +39,17 @@
  * Numerics: nf4_pack and nf4_unpack are exact (bit-for-bit defined below).
  * The products accumulate in fp32.  On the vector-ALU kernel (M <= 2, and
  * M = 3 or 4 on matrices of more than 5120 rows) the levels are f16 and each
- * activation block is scaled by a power of two into f16; on the MFMA kernels
- * (every other M, and nf4_gemm_prefill) the levels are split into bf16 hi + lo
- * and the bf16 activations are used as they are.  Per output element
- * |Y - Y_exact| <= 2e-3 * sum_k |w~(n,k) X[m][k]| + 1e-5 for finite inputs whose
- * products stay in range.  Results are deterministic: the same call on the same
- * device gives the same bits.
+ * 32-value activation block is scaled by a power of two into f16 where that is
+ * exact (every non-zero value of the block within 2^28 of its largest in
+ * binary exponent); a wavefront whose blocks are not all exact in f16 computes
+ * every weight as f16 level x fp32 scale (exact) times the bf16 activation in
+ * fp32 instead.  On the MFMA kernels (every other M, and nf4_gemm_prefill) the
+ * levels are split into bf16 hi + lo and the bf16 activations are used as they
+ * are.  Per output element
+ *   |Y - Y_exact| <= 2e-3 * sum_k |w~(n,k) X[m][k]| + 1e-5
+ * for finite inputs with every |X[m][k]| <= 2^120 and every
+ * sum_k |w~(n,k) X[m][k]| <= 2^120 (w~ = the dequantized weight).  Results are
+ * deterministic: the same call on the same device gives the same bits.
  */
 #ifndef NF4_H
 #define NF4_H
@@ -150,7 +157,7 @@ int nf4_gemm_smallm_ws(const uint8_t *codes, const uint16_t *scales, int64_t N, 
  * s(n,k/64) * X[m][k], for any batch 1 <= M with M * K < 2^30 (prefill chunks
  * beyond 32 positions), on 32 x 32 x 16 bf16 MFMA tiles of 64 x 64 to 128 x 128
  * outputs per workgroup.  Source: deep-fold README, "Method" (prefill on the
- * NF4 matrix-core product); Trapetum home page, "The fine print" (at prefill
+ * NF4 matrix-core product); Trapetum overview, "The fine print" (at prefill
  * sizes the product is bound by arithmetic, not by the weight stream).
  * Alignment: codes 16 bytes, scales 2, X 16, Y 4.  Errors: NF4_ERANGE for
  * M < 1 or M * K >= 2^30, otherwise as nf4_gemm_smallm.
@@ -193,17 +200,20 @@ int nf4_gemm_prefill_ws(const uint8_t *codes, const uint16_t *scales, int64_t N,
  *  - out: device bf16 bits [T][K].  T = 0 is valid and writes nothing.
  * Alignment: codes 4 bytes, scales 2, ids 8, out 16.  Errors: NF4_EINVAL for a
  * null pointer or T < 0, NF4_ERANGE if T is too large for one launch
- * (> 2^31 / ceil(K / 2048)), plus the shape rules of every call.
+ * (T > 8 * floor(floor((2^32 - 1) / 256) / ceil(K / 2048)), e.g. 134217720 rows
+ * for K <= 2048), plus the shape rules of every call; all checked before the
+ * status word is cleared.
  */
 int nf4_embed(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
               const int64_t *ids, int64_t T, uint16_t *out, int32_t *dev_status,
               void *stream);
 
 /*
- * CopyRing -- products over packed matrices held in pinned host memory,
- * streamed through two reusable device slots.  Source: deep-fold README,
- * "Method" (models exceeding the GPU budget: selected packed matrices stream
- * from pinned host memory through two reusable GPU slots into the same kernel).
+ * CopyRing -- products over packed matrices held in pinned host memory, staged
+ * through two device slots used in turn.  Source: deep-fold README, "Method",
+ * execution-path table and Figure 1 (for models larger than the card, some
+ * packed matrices stay in page-locked host memory and are copied into one of two
+ * device slots, where the same product kernel reads them).
  *
  * nf4_ring_create: slot0 / slot1 are caller-owned device buffers of slot_bytes
  * each (256-byte aligned); compute_stream and copy_stream are two hipStreams
@@ -226,7 +236,8 @@ int nf4_embed(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K
  * NF4_EDEVICE if the current device is not the ring's; the shape and alignment
  * rules of nf4_gemm_smallm otherwise.
  *
- * nf4_ring_slot_bytes: bytes a slot needs for an N x K matrix (-1 if invalid).
+ * nf4_ring_slot_bytes: bytes a slot needs for an N x K matrix (-1 if the shape
+ * is invalid or beyond the limits of the product calls).
  */
 typedef struct nf4_ring nf4_ring;
 int nf4_ring_create(nf4_ring **ring, void *slot0, void *slot1, int64_t slot_bytes,

@@ -13,6 +13,8 @@ import torch
 import oracle
 import workloads as wl
 
+import gpu_guard as guard
+
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
@@ -43,11 +45,40 @@ def _check_product(Y_gpu, Y_ref, A, what):
 
 def _pack_gpu(nf4, W):
     N, K = W.shape
-    codes, scales = nf4.empty_packed(N, K, W.device)
+    cbuf, codes = guard.alloc((N, K // 2), torch.uint8, W.device)
+    sbuf, scales = guard.alloc((N, K // 64), torch.int16, W.device)
     st = torch.full((1,), -7, dtype=torch.int32, device=W.device)
     nf4.nf4_pack(W, codes, scales, st)
     torch.cuda.synchronize()
+    guard.check(cbuf, "pack codes")
+    guard.check(sbuf, "pack scales")
     return codes, scales, int(st.item())
+
+
+def _guarded_product(nf4, codes, scales, X, via_gemv=False):
+    """Y = X . dequant^T through the C ABI (gemv, small-batch with a workspace
+    where the plan splits, or prefill tiles beyond 32 rows), with guard bands
+    around Y and the workspace."""
+    M, K = X.shape
+    N = codes.shape[0]
+    ybuf, Y = guard.alloc((M, N), torch.float32, X.device)
+    wbuf = None
+    if via_gemv:
+        nf4.nf4_gemv(codes, scales, X[0], Y.view(-1))
+    else:
+        big = M > nf4.MAX_M
+        need = (nf4.prefill_workspace_bytes if big else nf4.smallm_workspace_bytes)(N, K, M)
+        ws = None
+        if need:
+            wbuf, ws = guard.alloc(need, torch.uint8, X.device, fill=0)
+            wbuf[:guard.GUARD] = guard.SENTINEL
+            wbuf[guard.GUARD + need:] = guard.SENTINEL
+        (nf4.nf4_gemm_prefill_ws if big else nf4.nf4_gemm_smallm_ws)(codes, scales, X, Y, ws)
+    torch.cuda.synchronize()
+    guard.check(ybuf, f"Y of M={M} N={N} K={K}")
+    if wbuf is not None:
+        guard.check(wbuf, f"workspace of M={M} N={N} K={K}")
+    return Y
 
 
 def _u16(t):
@@ -113,8 +144,10 @@ def test_unpack_bit_exact(nf4, N, K):
     ref_p, ref_s, _ = _host_pack(W)
     codes = torch.from_numpy(ref_p).to(DEV)
     scales = torch.from_numpy(ref_s.view(np.int16)).to(DEV)
-    Wt = nf4.unpack(codes, scales, K)
+    wbuf, Wt = guard.alloc((N, K), torch.float32, DEV)
+    nf4.nf4_unpack(codes, scales, Wt)
     torch.cuda.synchronize()
+    guard.check(wbuf, "unpack W_out")
     ref = oracle.dequant_f32(ref_p, ref_s)
     assert np.array_equal(Wt.cpu().numpy().view(np.uint32), ref.view(np.uint32))
 
@@ -126,11 +159,7 @@ def _product_case(nf4, M, N, K, sigma=0.02, seed=0, via_gemv=None):
     codes, scales, st = _pack_gpu(nf4, W)
     ref_p, ref_s, _ = _host_pack(W)
     assert np.array_equal(codes.cpu().numpy(), ref_p)
-    if via_gemv or (via_gemv is None and M == 1):
-        Y = nf4.gemv(codes, scales, X[0])
-    else:
-        Y = nf4.gemm(codes, scales, X)
-    torch.cuda.synchronize()
+    Y = _guarded_product(nf4, codes, scales, X, via_gemv or (via_gemv is None and M == 1))
     Yr, A = oracle.gemm(ref_p, ref_s, wl.bf16_bits(X))
     _check_product(Y, Yr, A, f"M={M} N={N} K={K}")
     return codes, scales, X, Y
@@ -241,6 +270,80 @@ def test_activation_range_extremes(nf4):
         _check_product(Y, Yr, A, f"range M={M}")
 
 
+def _planted_range_case(nf4, M, N, K, ratios, units=None, seed=0, base=1.0):
+    """Activations whose 32-value units each hold one entry `ratio` times larger
+    than the rest, planted on a column whose weights are all exactly zero (code 7,
+    the zero level): the small entries then carry the whole sum.  `units`
+    restricts the planted units (default: every unit); ratios cycle over
+    (row, unit); every activation is first multiplied by `base`."""
+    W = wl.weights(N, K, 0.02, seed=seed * 101 + N + K, device=DEV).cpu()
+    X = wl.activations(M, K, seed=seed * 103 + M + K).float() * base
+    U = K // 32
+    units = range(U) if units is None else units
+    planted = []
+    for m in range(M):
+        for j, u in enumerate(units):
+            k0 = 32 * u + (7 * u + 3 * m) % 32
+            W[:, k0] = 0.0
+            r = ratios[(j + m) % len(ratios)]
+            X[m, k0] = (1.5 if (u + m) % 2 else -1.5) * r * base
+            planted.append((m, k0))
+    Xb = X.to(torch.bfloat16)
+    for m, k0 in planted:  # the planted entry is the unit's largest, exactly
+        assert abs(float(Xb[m, k0])) == abs(float(X[m, k0]))
+    codes, scales, st = _pack_gpu(nf4, W.to(DEV))
+    assert st == 0
+    ref_p, ref_s, _ = _host_pack(W)
+    assert np.array_equal(codes.cpu().numpy(), ref_p)
+    assert np.all(oracle.unpack_codes(ref_p)[:, [k for _, k in planted]] == 7)
+    Y = _guarded_product(nf4, codes, scales, Xb.to(DEV))
+    Yr, A = oracle.gemm(ref_p, ref_s, wl.bf16_bits(Xb))
+    _check_product(Y, Yr, A, f"planted range M={M} N={N} K={K} ratios={ratios}")
+    return Y, Yr
+
+
+@pytest.mark.parametrize("M", [1, 2, 4])
+def test_activation_range_planted_on_zero_weights(nf4, M):
+    """Per-unit activation ranges of 2^20, 2^26 (held exactly by the per-unit f16
+    shift) and 2^30, 2^40, 2^100 (beyond it: the exact fp32 form), with the large
+    entry on a zero-level weight, at M = 1, 2 and 4 on 6144 rows (all three on
+    the vector-ALU kernel)."""
+    ratios = [2.0 ** 20, 2.0 ** 26, 2.0 ** 30, 2.0 ** 40, 2.0 ** 100]
+    _planted_range_case(nf4, M, 6144, 4096, ratios, seed=M)
+    # the same at a larger magnitude: the rest ~ 2^60, the planted entry 2^100
+    # above the usual scale, so the sums stay within fp32 only if nothing is
+    # summed before its scale is applied
+    Y, Yr = _planted_range_case(nf4, M, 6144, 1024, [2.0 ** 40], seed=10 + M, base=2.0 ** 60)
+    assert np.isfinite(Y.cpu().numpy()).all()
+
+
+def test_activation_range_in_one_slice_only(nf4):
+    """K = 16384 at M = 1 runs four K-slices: only the waves whose slice holds a
+    planted unit take the exact fp32 form, the others the f16 form; the slices'
+    sums meet in one output."""
+    U = 16384 // 32
+    _planted_range_case(nf4, 1, 6144, 16384, [2.0 ** 40], units=range(0, U // 4, 16), seed=5)
+    _planted_range_case(nf4, 1, 6144, 16384, [2.0 ** 30], units=[U - 1], seed=6)
+
+
+def test_activation_range_with_bf16_subnormals(nf4):
+    """bf16 subnormal activations beside normal ones in one unit (both forms of
+    the per-unit check): within tolerance at M = 1, 2."""
+    N, K = 6144, 2048
+    W = wl.weights(N, K, 0.02, seed=31, device=DEV)
+    codes, scales, _ = _pack_gpu(nf4, W)
+    ref_p, ref_s, _ = _host_pack(W)
+    for M in (1, 2):
+        X = wl.activations(M, K, seed=32 + M).float()
+        X[:, 5::64] = 3e-39   # subnormal in bf16 (below 2^-126)
+        X[:, 9::128] *= 2.0 ** -100
+        Xb = X.to(torch.bfloat16)
+        Y = nf4.gemm(codes, scales, Xb.to(DEV))
+        torch.cuda.synchronize()
+        Yr, A = oracle.gemm(ref_p, ref_s, wl.bf16_bits(Xb))
+        _check_product(Y, Yr, A, f"subnormal activations M={M}")
+
+
 # ------------------------------------------------------------------ full sizes, sampled rows
 def _sampled_rows(N, count, seed):
     rng = np.random.default_rng(seed)
@@ -254,8 +357,7 @@ def _full_size_case(nf4, set_, proj, N, K, M):
     X = wl.activations(M, K, wl.seed_for(set_.name, 0, proj, "x"), device=DEV)
     codes, scales, st = _pack_gpu(nf4, W)
     assert st == 0
-    Y = nf4.gemv(codes, scales, X[0]) if M == 1 else nf4.gemm(codes, scales, X)
-    torch.cuda.synchronize()
+    Y = _guarded_product(nf4, codes, scales, X, via_gemv=M == 1)
     rows = _sampled_rows(N, 48, N + K + M)
     Wr = W[torch.from_numpy(rows).to(DEV)].cpu().numpy()
     ref_p, ref_s, _ = oracle.quantize_pack(Wr)
