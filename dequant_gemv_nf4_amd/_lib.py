@@ -199,17 +199,37 @@ def nf4_gemm_smallm_ws(codes, scales, X, Y, workspace, stream=None):
 # one workspace per (device, stream): calls sharing one must not overlap, and
 # calls on one stream never do
 _workspaces = {}
+# Workspaces replaced by a larger one stay allocated for the life of the
+# process: a HIP graph captured earlier still holds their address, and work
+# already enqueued may still use them.  (Each replacement at least doubles the
+# size, so the kept ones add up to less than the current one.)
+_retired = []
 
 
 def workspace_for(device, nbytes, stream=None):
     """A zero-initialised workspace of at least nbytes for calls on `stream`
-    (default: the current stream) of `device`, kept and reused."""
+    (default: the current stream) of `device`, kept and reused.  A new one is
+    allocated and zeroed on that stream, so the zeroing is ordered before the
+    call that receives it."""
     device = torch.device(device)
-    key = (device.index, _stream(device, stream).value)
+    if device.index is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    handle = _stream(device, stream).value
+    key = (device.index, handle)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
-        _workspaces[key] = ws
+        size = max(nbytes, 1 << 16, 2 * ws.numel() if ws is not None else 0)
+        if isinstance(stream, torch.cuda.Stream):
+            ts = stream
+        elif stream is None:
+            ts = torch.cuda.current_stream(device)
+        else:
+            ts = torch.cuda.ExternalStream(handle, device=device)
+        with torch.cuda.device(device), torch.cuda.stream(ts):
+            new = torch.zeros(size, dtype=torch.uint8, device=device)
+        if ws is not None:
+            _retired.append(ws)
+        _workspaces[key] = ws = new
     return ws
 
 

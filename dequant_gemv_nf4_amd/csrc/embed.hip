@@ -120,9 +120,13 @@ hipError_t launch_embed(const uint8_t *codes, const uint16_t *scales, int64_t N,
   return hipGetLastError();
 }
 
+// A dispatch covers at most 2^32 - 1 work-items per dimension, so at most
+// floor((2^32 - 1) / 256) blocks; T rows take ceil(T / rpt) * bpr blocks, with
+// rpt = 8 rows per thread at every T near the limit.
 int64_t embed_max_rows(int64_t K) {
   const int64_t bpr = ((K >> 3) + kEmbedThreads - 1) / kEmbedThreads;
-  return ((int64_t(1) << 31) - 1) / bpr;
+  const int64_t max_blocks = ((int64_t(1) << 32) - 1) / kEmbedThreads;
+  return 8 * (max_blocks / bpr);
 }
 
 }  // namespace nf4

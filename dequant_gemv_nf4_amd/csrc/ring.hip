@@ -1,7 +1,9 @@
 // ring.hip -- CopyRing: products over packed matrices that live in pinned host
-// memory, streamed through two reusable device slots (deep-fold README,
-// "Method": models that exceed the GPU budget stream selected packed matrices
-// from pinned host memory through two reusable GPU slots into the same kernel).
+// memory, staged through a pair of device buffers that are used in turn
+// (deep-fold README, "Method", execution-path table and Figure 1: when a model
+// does not fit on the card, some of its packed matrices stay in page-locked host
+// memory and are copied into one of two device slots before the unchanged
+// product kernel runs on them).
 //
 // Each nf4_ring_gemm call takes the next slot (0, 1, 0, ...), and enqueues
 //   copy stream:    wait until the slot's previous product has finished reading
@@ -130,7 +132,9 @@ int nf4_ring_gemm(nf4_ring *r, const uint8_t *host_codes, const uint16_t *host_s
 }
 
 int64_t nf4_ring_slot_bytes(int64_t N, int64_t K) {
+  // the shape limits of every product call, checked before any arithmetic
   if (N <= 0 || K <= 0 || K % NF4_GROUP != 0) return -1;
+  if (K > NF4_MAX_K || N >= (int64_t(1) << 31) || N * (K / 2) >= (int64_t(1) << 31)) return -1;
   return scale_offset(N, K) + N * (K / NF4_GROUP) * 2;
 }
 

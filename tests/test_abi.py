@@ -187,6 +187,18 @@ def test_embed_validation(lib):
     assert lib.nf4_embed(P, P, 4, 64, P, 2 ** 31, P, NULL, NULL) == ERANGE
 
 
+@pytest.mark.parametrize("K", [64, 2048, 2112, 4096, 32768])
+def test_embed_row_limit_fits_one_dispatch(lib, K):
+    """T beyond what one dispatch's 2^32 - 1 work-items cover is refused before
+    anything is enqueued (status word included)."""
+    bpr = -(-(K // 8) // 256)
+    limit = 8 * (((2 ** 32 - 1) // 256) // bpr)
+    # the launch grid at the limit: ceil(T / 8) blocks per row-block, 256 threads each
+    assert -(-limit // 8) * bpr * 256 <= 2 ** 32 - 1
+    assert lib.nf4_embed(P, P, 4, K, P, limit + 1, P, NULL, NULL) == ERANGE
+    assert lib.nf4_embed(P, P, 4, K, P, limit + 1, P, P, NULL) == ERANGE
+
+
 def test_ring_validation_without_a_device(lib):
     out = ctypes.c_void_p()
     assert lib.nf4_ring_create(None, P, P, 1024, NULL, NULL) == EINVAL
@@ -200,3 +212,7 @@ def test_ring_validation_without_a_device(lib):
     assert lib.nf4_ring_slot_bytes(4, 64) == 256 + 4 * 2
     assert lib.nf4_ring_slot_bytes(4096, 4096) == 4096 * 2048 + 4096 * 64 * 2
     assert lib.nf4_ring_slot_bytes(4, 65) == -1
+    # beyond the product limits: refused, not computed (the arithmetic would overflow)
+    assert lib.nf4_ring_slot_bytes(2 ** 61, 2 ** 61) == -1
+    assert lib.nf4_ring_slot_bytes(4, 32768 + 64) == -1
+    assert lib.nf4_ring_slot_bytes(2 ** 31, 64) == -1

@@ -9,6 +9,8 @@ import torch
 import oracle
 import workloads as wl
 
+import gpu_guard as guard
+
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
@@ -32,10 +34,11 @@ def _run(nf4, packed, scales, ids):
     sc = torch.from_numpy(scales.view(np.int16)).to(DEV)
     K = packed.shape[1] * 2
     idt = torch.from_numpy(np.asarray(ids, np.int64)).to(DEV)
-    out = torch.full((idt.numel(), K), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    buf, out = guard.alloc((idt.numel(), K), torch.bfloat16, DEV)
     st = torch.full((1,), -7, dtype=torch.int32, device=DEV)
     nf4.nf4_embed(codes, sc, K, idt, out, st)
     torch.cuda.synchronize()
+    guard.check(buf, "embed out")
     return _bits(out), int(st.item())
 
 

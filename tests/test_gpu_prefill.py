@@ -12,6 +12,8 @@ import torch
 import oracle
 import workloads as wl
 
+import gpu_guard as guard
+
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
@@ -36,9 +38,10 @@ def _pack(nf4, W):
 
 
 def _prefill(nf4, codes, scales, X):
-    Y = torch.empty((X.shape[0], codes.shape[0]), dtype=torch.float32, device=X.device)
+    buf, Y = guard.alloc((X.shape[0], codes.shape[0]), torch.float32, X.device)
     nf4.nf4_gemm_prefill(codes, scales, X, Y)
     torch.cuda.synchronize()
+    guard.check(buf, "prefill Y")
     return Y
 
 
@@ -183,10 +186,13 @@ def test_prefill_full_size_8b(nf4, M):
 
 
 # ------------------------------------------------------------------ workgroup K-splits
-def _prefill_ws(nf4, codes, scales, X, ws):
-    Y = torch.empty((X.shape[0], codes.shape[0]), dtype=torch.float32, device=X.device)
+def _prefill_ws(nf4, codes, scales, X, ws, ws_buf=None):
+    buf, Y = guard.alloc((X.shape[0], codes.shape[0]), torch.float32, X.device)
     nf4.nf4_gemm_prefill_ws(codes, scales, X, Y, ws)
     torch.cuda.synchronize()
+    guard.check(buf, "prefill_ws Y")
+    if ws_buf is not None:
+        guard.check(ws_buf, "prefill_ws workspace")
     return Y
 
 
@@ -197,10 +203,12 @@ def test_prefill_split_matches_oracle_and_repeats(nf4, M, N, K):
     W = wl.weights(N, K, 0.02, seed=N * 3 + K + M, device=DEV)
     X = wl.activations(M, K, seed=N + K * 5 + M, device=DEV)
     codes, scales = _pack(nf4, W)
-    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=DEV)
-    Y1 = _prefill_ws(nf4, codes, scales, X, ws)
-    Y2 = _prefill_ws(nf4, codes, scales, X, ws)
-    Y3 = _prefill_ws(nf4, codes, scales, X, ws)
+    ws_buf, ws = guard.alloc(max(need, 256), torch.uint8, DEV, fill=0)
+    ws_buf[:guard.GUARD] = guard.SENTINEL
+    ws_buf[guard.GUARD + ws.numel():] = guard.SENTINEL
+    Y1 = _prefill_ws(nf4, codes, scales, X, ws, ws_buf)
+    Y2 = _prefill_ws(nf4, codes, scales, X, ws, ws_buf)
+    Y3 = _prefill_ws(nf4, codes, scales, X, ws, ws_buf)
     # the same bits on every call: the counters re-arm after each one
     assert torch.equal(Y1, Y2) and torch.equal(Y1, Y3)
     rows = _rows(N, 64, M + N) if N * K > 2 ** 22 else np.arange(N)

@@ -9,6 +9,8 @@ import torch
 import oracle
 import workloads as wl
 
+import gpu_guard as guard
+
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
@@ -41,10 +43,13 @@ def _check(Y, Yr, A, what):
                     f"{[(tuple(i), Y[tuple(i)], Yr[tuple(i)]) for i in idx]}")
 
 
-def _run_ws(nf4, codes, scales, X, ws):
-    Y = torch.empty((X.shape[0], codes.shape[0]), dtype=torch.float32, device=DEV)
+def _run_ws(nf4, codes, scales, X, ws, ws_buf=None):
+    buf, Y = guard.alloc((X.shape[0], codes.shape[0]), torch.float32, DEV)
     nf4.nf4_gemm_smallm_ws(codes, scales, X, Y, ws)
     torch.cuda.synchronize()
+    guard.check(buf, "smallm_ws Y")
+    if ws_buf is not None:
+        guard.check(ws_buf, "smallm_ws workspace")
     return Y
 
 
@@ -64,10 +69,12 @@ def test_split_matches_oracle_and_repeats(nf4, M, N, K):
     W = wl.weights(N, K, 0.02, seed=N + K + M, device=DEV)
     X = wl.activations(M, K, seed=3 * N + K + M, device=DEV)
     codes, scales = _pack(nf4, W)
-    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=DEV)
-    Y1 = _run_ws(nf4, codes, scales, X, ws)
-    Y2 = _run_ws(nf4, codes, scales, X, ws)
-    Y3 = _run_ws(nf4, codes, scales, X, ws)
+    ws_buf, ws = guard.alloc(max(need, 256), torch.uint8, DEV, fill=0)
+    ws_buf[:guard.GUARD] = guard.SENTINEL
+    ws_buf[guard.GUARD + ws.numel():] = guard.SENTINEL
+    Y1 = _run_ws(nf4, codes, scales, X, ws, ws_buf)
+    Y2 = _run_ws(nf4, codes, scales, X, ws, ws_buf)
+    Y3 = _run_ws(nf4, codes, scales, X, ws, ws_buf)
     # the same bits on every call: the counters re-arm after each one
     assert torch.equal(Y1, Y2) and torch.equal(Y1, Y3)
     rows = _rows(N, 96, M * N + K) if N * K > 4096 * 1024 else np.arange(N)
@@ -157,3 +164,48 @@ def test_one_workspace_across_shapes_and_entry_points(nf4):
         torch.cuda.synchronize()
         assert torch.equal(Y, Yf), f"{entry} M={M} N={N} K={K} on the shared workspace"
         assert int(shared[:4096].count_nonzero().item()) == 0
+
+
+def test_captured_workspace_survives_a_larger_call(nf4):
+    """gemm() captured in a HIP graph on a stream keeps the workspace it was
+    captured with even after a larger call on the same stream replaces the
+    stream's workspace: the memory is not handed out again, so replays (with
+    fresh allocations filled with junk in between) still match the oracle and
+    the eager bits."""
+    s = torch.cuda.Stream()
+    N, K, M = 4096, 4096, 32
+    codes, scales = _pack(nf4, wl.weights(N, K, 0.02, seed=95, device=DEV))
+    X = wl.activations(M, K, seed=96, device=DEV)
+    Nb, Kb = 4096, 14336
+    assert 0 < nf4.smallm_workspace_bytes(N, K, M) < nf4.smallm_workspace_bytes(Nb, Kb, M)
+    cb, sb = _pack(nf4, wl.weights(Nb, Kb, 0.02, seed=97, device=DEV))
+    Xb = wl.activations(M, Kb, seed=98, device=DEV)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ref = nf4.gemm(codes, scales, X)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        Yg = nf4.gemm(codes, scales, X)
+    with torch.cuda.stream(s):
+        Ybig = nf4.gemm(cb, sb, Xb)       # replaces the stream's workspace
+        junk = [torch.full((1 << 20,), -1, dtype=torch.int32, device=DEV) for _ in range(8)]
+    s.synchronize()
+    torch.cuda.synchronize()
+    rows = _rows(N, 96, 4242)
+    r = torch.from_numpy(rows).to(DEV)
+    ref_p, ref_s, _ = oracle.quantize_pack(
+        wl.weights(N, K, 0.02, seed=95, device=DEV)[r].cpu().numpy())
+    Yr, A = oracle.gemm(ref_p, ref_s, wl.bf16_bits(X))
+    for i in range(3):
+        with torch.cuda.stream(s):
+            Yg.zero_()
+            g.replay()
+        s.synchronize()
+        assert torch.equal(Yg, ref), i
+        _check(Yg[:, r], Yr, A, f"replay {i} after a larger call")
+    rb = torch.from_numpy(_rows(Nb, 64, 4343)).to(DEV)
+    pb, psb, _ = oracle.quantize_pack(wl.weights(Nb, Kb, 0.02, seed=97, device=DEV)[rb].cpu().numpy())
+    Ybr, Ab = oracle.gemm(pb, psb, wl.bf16_bits(Xb))
+    _check(Ybig[:, rb], Ybr, Ab, "the larger call")
+    del junk
