@@ -4,7 +4,7 @@
 // Computes Y[m][n] = sum_k L[code(n,k)] * s(n,k/64) * X[m][k].  Sources:
 // deep-fold README, "Method" (prefill runs the NF4 product on chunks of
 // positions, the weights rebuilt into matrix-core register fragments and never
-// written out); Trapetum home page, "The fine print" (prefill saves memory
+// written out); Trapetum overview, "The fine print" (prefill saves memory
 // traffic, not time: once M is large the product is bound by the matrix cores,
 // not by the weight stream).
 //

@@ -1,8 +1,8 @@
 """Summaries of rocprofv3 result databases (rocpd SQLite) for the NF4 kernels.
 
-    python -m dequant_gemv_nf4_amd.rocpd_summary trace  <results.db> [name-filter] [prev]
-    python -m dequant_gemv_nf4_amd.rocpd_summary pmc    <results.db> [name-filter] [prev]
-    python -m dequant_gemv_nf4_amd.rocpd_summary copies <results.db> [name-filter]
+    python rocpd_summary.py trace  <results.db> [name-filter] [prev]
+    python rocpd_summary.py pmc    <results.db> [name-filter] [prev]
+    python rocpd_summary.py copies <results.db> [name-filter]
 
 `trace` groups dispatches by (kernel, grid, workgroup) and prints count, mean,
 median, p10 and p90 duration.  `pmc` prints the mean of every collected counter

@@ -1,6 +1,7 @@
-"""GPU checks of CopyRing (nf4_ring_*, deep-fold README "Method": packed
-matrices stream from pinned host memory through two reusable GPU slots into
-the same kernel): every product equals the resident product bit for bit and the
+"""GPU checks of CopyRing (nf4_ring_*; deep-fold README, "Method", execution-path
+table and Figure 1: packed matrices kept in page-locked host memory are copied
+into one of two device slots, used in turn, and multiplied there by the
+unchanged kernel): every product equals the resident product bit for bit and the
 oracle within tolerance, over sequences long enough to reuse both slots many
 times; argument errors."""
 import numpy as np

@@ -86,10 +86,34 @@ def test_generators_are_seeded_and_shaped():
 
 
 def test_cpu_baseline_leg_reports_the_contract_keys():
-    out = bench.cpu_baseline(wl.SINGLE_4096, 1, 0.05)
-    assert set(out) >= {"value", "unit", "cores", "kind", "sample"}
-    assert out["kind"] == "oracle" and out["cores"] == 1 and out["value"] > 0
+    out = bench.cpu_baseline(wl.SINGLE_4096, 1, 0.05, threads=3)
+    assert set(out) >= {"value", "unit", "cores", "kind", "sample", "one_thread", "host"}
+    assert out["kind"] == "oracle" and out["cores"] == 3 and out["value"] > 0
+    assert out["one_thread"]["cores"] == 1 and out["one_thread"]["value"] > 0
     assert np.isfinite(out["value"])
+    assert out["host"]["nproc"] >= 1 and out["host"]["cpu_model"]
+
+
+def test_cpu_baseline_threads_default_to_the_usable_cores():
+    out = bench.cpu_baseline(wl.SINGLE_4096, 1, 0.05)
+    assert 1 <= out["cores"] <= bench.CPU_THREAD_CAP
+    assert out["cores"] == min(bench.CPU_THREAD_CAP, bench.host_info()["cpus_usable"])
+
+
+def test_stats_and_dtype_labels():
+    s = bench.stats([5.0, 1.0, 3.0, 2.0, 4.0])
+    assert s["median"] == 3.0 and s["min"] == 1.0 and s["max"] == 5.0 and s["n"] == 5
+    assert s["p10"] <= s["median"] <= s["p90"]
+    assert bench.dtype_label(1, [(4096, 4096)]) == "nf4-w/bf16-x/f16-dot/fp32-acc"
+    assert bench.dtype_label(4, [(6144, 4096), (4096, 4096)]) == \
+        "nf4-w/bf16-x/bf16-mfma+f16-dot/fp32-acc"
+    assert bench.dtype_label(64, [(4096, 4096)]) == "nf4-w/bf16-x/bf16-mfma/fp32-acc"
+
+
+def test_build_record_matches_the_sources():
+    from dequant_gemv_nf4_amd import build as nb
+    info = json.load(open(nb.BUILD_INFO))
+    assert info["sources_sha256"] == nb.sources_sha256(), "library built from other sources"
 
 
 @pytest.mark.parametrize("M,N,K,name", [
@@ -109,7 +133,7 @@ def test_rocpd_summary_splits_by_preceding_kernel(tmp_path):
     """Two shapes that share a kernel and a grid (o after q|k|v, down after
     gate|up) come apart when groups are keyed by the kernel dispatched before."""
     import sqlite3
-    from dequant_gemv_nf4_amd import rocpd_summary as rs
+    import rocpd_summary as rs
     db = sqlite3.connect(tmp_path / "r.db")
     db.execute("create table kernels (name text, grid_x int, workgroup_x int, start int, end int)")
     db.execute("create table counters_collection (dispatch_id int, kernel_name text, "
