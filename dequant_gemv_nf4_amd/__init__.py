@@ -24,11 +24,13 @@ from ._lib import (  # noqa: F401
     gemm,
     gemv,
     lib_path,
+    noalloc_max_bytes,
     nf4_codebook,
     nf4_embed,
     nf4_gemm_prefill,
     nf4_gemm_prefill_ws,
     nf4_gemm_smallm,
+    nf4_gemm_smallm_noalloc,
     nf4_gemm_smallm_ws,
     nf4_gemv,
     nf4_pack,

@@ -49,6 +49,10 @@ def _load():
     L.nf4_gemm_smallm_ws.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, i64, vp]
     L.nf4_gemm_smallm_workspace_bytes.argtypes = [i64, i64, i64]
     L.nf4_gemm_smallm_workspace_bytes.restype = ctypes.c_int64
+    L.nf4_gemm_smallm_noalloc.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp]
+    L.nf4_gemm_smallm_noalloc.restype = ctypes.c_int
+    L.nf4_gemm_smallm_noalloc_max_bytes.argtypes = []
+    L.nf4_gemm_smallm_noalloc_max_bytes.restype = ctypes.c_int64
     L.nf4_gemm_prefill_ws.argtypes = [vp, vp, i64, i64, vp, i64, vp, vp, i64, vp]
     L.nf4_gemm_prefill_workspace_bytes.argtypes = [i64, i64, i64]
     L.nf4_gemm_prefill_workspace_bytes.restype = ctypes.c_int64
@@ -194,6 +198,28 @@ def nf4_gemm_smallm_ws(codes, scales, X, Y, workspace, stream=None):
         _check("nf4_gemm_smallm_ws", _load().nf4_gemm_smallm_ws(
             _ptr(codes), _ptr(scales), N, K, _ptr(X), M, _ptr(Y), _ptr(workspace), nbytes,
             _stream(X.device, stream)))
+
+
+def noalloc_max_bytes():
+    """Size of the library-owned scratch behind nf4_gemm_smallm_noalloc."""
+    return int(_load().nf4_gemm_smallm_noalloc_max_bytes())
+
+
+def nf4_gemm_smallm_noalloc(codes, scales, X, Y, stream=None):
+    """nf4_gemm_smallm_ws with the library's own per-device scratch instead of a
+    workspace: no allocation anywhere in the call.  Calls that overlap on one GPU
+    race on that scratch."""
+    _need(codes, "codes", (torch.uint8,), (2,))
+    _need(scales, "scales", _U16 + (torch.float16,))
+    _need(X, "X", _BF16, (1, 2))
+    _need(Y, "Y", (torch.float32,))
+    M, K = (1, X.shape[0]) if X.dim() == 1 else X.shape
+    N = _nk(codes, scales, K)
+    if Y.numel() != M * N:
+        raise ValueError("Y must have M*N elements")
+    with torch.cuda.device(X.device):
+        _check("nf4_gemm_smallm_noalloc", _load().nf4_gemm_smallm_noalloc(
+            _ptr(codes), _ptr(scales), N, K, _ptr(X), M, _ptr(Y), _stream(X.device, stream)))
 
 
 # one workspace per (device, stream): calls sharing one must not overlap, and

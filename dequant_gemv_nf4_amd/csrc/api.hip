@@ -2,6 +2,7 @@
 // device check and kernel choice.  No allocation, no synchronization.
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/nf4.h"
 #include "nf4_device.h"
@@ -39,6 +40,42 @@ int check_shape(int64_t N, int64_t K) {
 }
 
 int launched(hipError_t e) { return e == hipSuccess ? NF4_OK : NF4_ELAUNCH; }
+
+// ---- the library-owned scratch of nf4_gemm_smallm_noalloc: one array per
+// device (each GPU the library runs on holds its own copy until the process
+// ends), in place of a caller workspace.  The host never passes `scratch`
+// itself to a kernel (in host code it is only a stand-in for the symbol): the
+// device address is looked up once per device with hipGetSymbolAddress and kept.
+constexpr int64_t kScratchBytes = int64_t(4) << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];  // device address of `scratch` per device, set once
+
+__global__ void clear_counters_kernel(uint32_t *p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// The device's scratch address, set up on the device's first call: the lookup,
+// then the counter area cleared by a kernel on the caller's stream (every
+// completed split call leaves the counters zero again).
+int scratch_for_current_device(void **out, hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return NF4_ERANGE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return NF4_ELAUNCH;
+    constexpr int n = nf4::kSplitCounters;
+    hipLaunchKernelGGL(clear_counters_kernel, dim3((n + 255) / 256), dim3(256), 0, stream,
+                       static_cast<uint32_t *>(p), n);
+    if (hipGetLastError() != hipSuccess) return NF4_ELAUNCH;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return NF4_OK;
+}
 
 }  // namespace
 
@@ -107,6 +144,30 @@ int nf4_gemm_smallm(const uint8_t *codes, const uint16_t *scales, int64_t N, int
   if (nf4::use_valu(N, K, m))
     return launched(nf4::launch_gemv_valu(codes, scales, N, K, X, m, Y, s));
   return launched(nf4::launch_gemm_mfma(codes, scales, N, K, X, m, Y, nullptr, 0, s));
+}
+
+int64_t nf4_gemm_smallm_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int nf4_gemm_smallm_noalloc(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                            const uint16_t *X, int64_t M, float *Y, void *stream) {
+  if (!codes || !scales || !X || !Y) return NF4_EINVAL;
+  if (int r = check_shape(N, K)) return r;
+  if (M < 1 || M > NF4_MAX_M) return NF4_ERANGE;
+  if (!aligned(codes, 16) || !aligned(scales, 2) || !aligned(X, 16) || !aligned(Y, 4))
+    return NF4_EALIGN;
+  const int64_t need = nf4_gemm_smallm_workspace_bytes(N, K, M);
+  if (need > kScratchBytes) return NF4_ERANGE;
+  if (int r = check_device()) return r;
+  const int m = (int)M;
+  hipStream_t s = (hipStream_t)stream;
+  if (nf4::use_valu(N, K, m))
+    return launched(nf4::launch_gemv_valu(codes, scales, N, K, X, m, Y, s));
+  void *ws = nullptr;
+  if (need > 0) {
+    if (int r = scratch_for_current_device(&ws, s)) return r;
+  }
+  return launched(nf4::launch_gemm_mfma(codes, scales, N, K, X, m, Y, ws,
+                                        need > 0 ? kScratchBytes : 0, s));
 }
 
 int64_t nf4_gemm_prefill_workspace_bytes(int64_t N, int64_t K, int64_t M) {

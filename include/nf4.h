@@ -153,6 +153,29 @@ int nf4_gemm_smallm_ws(const uint8_t *codes, const uint16_t *scales, int64_t N, 
                        int64_t workspace_bytes, void *stream);
 
 /*
+ * nf4_gemm_smallm_noalloc -- nf4_gemm_smallm_ws without a caller workspace and
+ * without any allocation: the K-split partial tiles and counters live in a
+ * library-owned device array of nf4_gemm_smallm_noalloc_max_bytes() bytes
+ * (4 MiB; every valid small-batch shape needs at most about 2 MiB), one per
+ * device, held until the process ends.  For callers that cannot allocate
+ * device memory at the point of the call: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same kernels, plans and
+ * bits as nf4_gemm_smallm_ws with a workspace.
+ *  - The first call on a device looks up the array's address (hipGetSymbolAddress)
+ *    and clears its counter area with a kernel on `stream`; make that first call
+ *    outside graph capture.  No call allocates or frees memory.
+ *  - Every call on one device shares that device's array and leaves its
+ *    counters zero: calls that overlap on one GPU (concurrent streams, or host
+ *    threads) race on it and must be serialized by the caller.
+ *  - Errors: as nf4_gemm_smallm; NF4_ERANGE if the shape would need more than
+ *    nf4_gemm_smallm_noalloc_max_bytes() of scratch.
+ * nf4_gemm_smallm_noalloc_max_bytes: the array's size in bytes.  Host only.
+ */
+int64_t nf4_gemm_smallm_noalloc_max_bytes(void);
+int nf4_gemm_smallm_noalloc(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                            const uint16_t *X, int64_t M, float *Y, void *stream);
+
+/*
  * nf4_gemm_prefill -- the same product, Y[m][n] = sum_k L[code(n,k)] *
  * s(n,k/64) * X[m][k], for any batch 1 <= M with M * K < 2^30 (prefill chunks
  * beyond 32 positions), on 32 x 32 x 16 bf16 MFMA tiles of 64 x 64 to 128 x 128
