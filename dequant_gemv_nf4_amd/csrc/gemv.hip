@@ -31,12 +31,16 @@
 // unit in fp32.
 //
 // Activations are converted once per workgroup: X is read in coalesced 16-byte
-// chunks, each 32-value unit is scaled by a power of two that puts its largest
-// |x| just under 2^15 (exact from bf16 down to 2^-29 of that maximum), converted
-// to f16 and staged in LDS with the shift; lanes then copy their units into
-// registers.  The shift is undone on the unit's fp32 partial.  Activation loads
-// are issued before the first code loads so that the set-up does not wait
-// behind them (loads return in order).
+// chunks, each 32-value unit is scaled by the power of two that puts its largest
+// |x| in [2^14, 2^15) and converted to f16 with integer operations on the bit
+// patterns (a saturating subtract of the exponent difference and a shift, two
+// values per instruction), then staged in LDS with its shift; lanes copy their
+// units into registers.  The shift is undone on the unit's fp32 partial.  A unit
+// whose values do not all land on f16 normals (a non-zero value more than 2^28
+// below the largest in binary exponent, or a largest below 2^-98) is staged as
+// zeros and handled by the exact pass after the row loop.  Activation loads are
+// issued before the first code loads so that the set-up does not wait behind
+// them (loads return in order).
 //
 // Reduction: per row, lanes are summed with DPP row operations in a fixed order;
 // row results wait in LDS and the S slices of a row are added in slice order
@@ -49,6 +53,7 @@
 namespace nf4 {
 
 typedef __fp16 fp16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(fp16x2_t, a), __builtin_bit_cast(fp16x2_t, b),
@@ -207,6 +212,7 @@ __global__ void __launch_bounds__(kThreads)
   uint32_t xh[M][UPL][16];
   float xf[M][UPL];  // 2^-shift of each unit
   uint4 *stage_x = reinterpret_cast<uint4 *>(stage);                 // [4][M][U]
+  const int q_elems = M * U;                                         // stage_x stride of q
   int *stage_sh = reinterpret_cast<int *>(stage + M * U * 64);       // [M][U]
   // (only the chunks a wave loaded: the loop is unrolled for the largest M K,
   // and work on unloaded chunks would cost the whole wave its set-up time)
@@ -215,28 +221,52 @@ __global__ void __launch_bounds__(kThreads)
     if (wave_chunk0 + j * kThreads < nchunks) {  // uniform per wave
       const int c = tid + j * kThreads;
       const uint4 v = xr[j];
-      uint32_t mx = max(max(bf16x2_absmax_bits(v.x), bf16x2_absmax_bits(v.y)),
-                        max(bf16x2_absmax_bits(v.z), bf16x2_absmax_bits(v.w)));
-      uint32_t mn = min(min(bf16x2_absmin_nz_bits(v.x), bf16x2_absmin_nz_bits(v.y)),
-                        min(bf16x2_absmin_nz_bits(v.z), bf16x2_absmin_nz_bits(v.w)));
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      u16x2 mag[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mag[e] = __builtin_bit_cast(u16x2, w[e] & 0x7fff7fffu);
+      const uint32_t pm = __builtin_bit_cast(
+          uint32_t, __builtin_elementwise_max(__builtin_elementwise_max(mag[0], mag[1]),
+                                              __builtin_elementwise_max(mag[2], mag[3])));
+      uint32_t mx = max(pm & 0xffffu, pm >> 16);  // the unit's largest |x|, bf16 bits
       mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0xB1, 0xf, 0xf, false));
       mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x4E, 0xf, 0xf, false));
-      mn = min(mn, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mn, 0xB1, 0xf, 0xf, false));
-      mn = min(mn, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mn, 0x4E, 0xf, 0xf, false));
+      // Scaling by 2^(141 - Emax) puts the largest in [2^14, 2^15): on the bit
+      // patterns, subtract (Emax - 29) << 7 from each magnitude (saturating, so
+      // zero stays zero) and shift left by 3 to the f16 exponent and mantissa
+      // fields.  Exact for a value of exponent E >= Emax - 28 (an f16 normal);
+      // a non-zero magnitude below that is "lost".
+      const uint32_t emax = mx >> 7;
+      const uint32_t bias = ((emax - 29u) << 7) & 0xffffu;
+      const u16x2 bias2 = __builtin_bit_cast(u16x2, bias * 0x10001u);
+      const u16x2 thr = __builtin_bit_cast(u16x2, (bias + 0x7fu) * 0x10001u);
+      uint32_t lost = 0;  // non-zero where 0 < |x| < 2^(Emax - 28 - 127)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        lost |= __builtin_bit_cast(
+            uint32_t, __builtin_elementwise_sub_sat(thr, mag[e] - (u16x2){1, 1}));
+      lost |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lost, 0xB1, 0xf, 0xf, false);
+      lost |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lost, 0x4E, 0xf, 0xf, false);
       if (c < nchunks) {  // nchunks is a multiple of 4: a quad is valid or not as a whole
-        const int sh = f16_range_shift(mx);
-        const bool wide = f16_unit_inexact(mx, mn);
+        // wide: some value would be lost, or the largest is below 2^-98 (the
+        // shift would leave the subtraction's range); all-zero units are exact
+        const bool wide = mx != 0 && (emax < 29u || lost != 0);
         const int q = c & 3;
         const int mu = c >> 2;  // m * U + u
-        const int m = mu / U;
-        const int u = mu - m * U;
         // a unit f16 cannot hold exactly is staged as zeros: the row loop adds
         // nothing for it, and the exact pass after the loop adds its terms
-        stage_x[(q * M + m) * U + u] =
-            wide ? make_uint4(0u, 0u, 0u, 0u)
-                 : make_uint4(bf16x2_to_f16x2(v.x, sh), bf16x2_to_f16x2(v.y, sh),
-                              bf16x2_to_f16x2(v.z, sh), bf16x2_to_f16x2(v.w, sh));
-        if (q == 0) stage_sh[mu] = wide ? kWideUnit : sh;
+        uint4 f = make_uint4(0u, 0u, 0u, 0u);
+        if (!wide) {
+          uint32_t h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            h[e] = __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(mag[e], bias2)
+                                                    << (u16x2){3, 3}) |
+                   (w[e] & 0x80008000u);
+          f = make_uint4(h[0], h[1], h[2], h[3]);
+        }
+        stage_x[q * q_elems + mu] = f;
+        if (q == 0) stage_sh[mu] = wide ? kWideUnit : (int)(141u - emax);
       }
     }
   }

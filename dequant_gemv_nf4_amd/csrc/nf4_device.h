@@ -119,48 +119,6 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-// Power-of-two shift that puts the largest of a set of bf16 magnitudes just
-// under 2^15 (mx = the largest |x| as bf16 bits without sign).
-__device__ __forceinline__ int f16_range_shift(uint32_t mx) {
-  int e = 0;
-  (void)frexpf(__uint_as_float(mx << 16), &e);  // max < 2^e
-  return 15 - e;
-}
-
-// two bf16 (one word) -> two f16 scaled by 2^sh (one word), nearest even
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w, int sh) {
-  const _Float16 lo = (_Float16)ldexpf(bf16_lo(w), sh);
-  const _Float16 hi = (_Float16)ldexpf(bf16_hi(w), sh);
-  return (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-}
-
-// largest |value| of the two bf16 in a word, as sign-less bf16 bits
-__device__ __forceinline__ uint32_t bf16x2_absmax_bits(uint32_t w) {
-  const uint32_t a = w & 0x7fff7fffu;
-  return max(a & 0xffffu, a >> 16);
-}
-
-// smallest non-zero |value| of the two bf16 in a word, as sign-less bf16 bits
-// (0xffff if both are zero)
-__device__ __forceinline__ uint32_t bf16x2_absmin_nz_bits(uint32_t w) {
-  const uint32_t a = w & 0x7fff7fffu;
-  const uint32_t lo = a & 0xffffu, hi = a >> 16;
-  return min(lo ? lo : 0xffffu, hi ? hi : 0xffffu);
-}
-
-// Whether a set of bf16 values (largest magnitude mx, smallest non-zero mn, as
-// sign-less bits) loses bits when scaled by f16_range_shift(mx) and converted to
-// f16.  The shift puts the largest value in [2^14, 2^15), so a value of biased
-// exponent E lands at or above 2^(E - Emax + 14); it is an f16 normal, and with
-// 8 significant bits exact, while E >= Emax - 28.  A bf16 subnormal is at least
-// 2^-133, i.e. counts as E = -6.  (Zero is exact; an all-zero set is not wide.)
-__device__ __forceinline__ bool f16_unit_inexact(uint32_t mx, uint32_t mn) {
-  const int emax = (int)(mx >> 7);
-  const int emin = (int)(mn >> 7) > 0 ? (int)(mn >> 7) : -6;
-  return mx != 0 && emin < emax - 28;
-}
-
 // ---------------------------------------------------------------------------
 // Wave reductions with DPP row operations plus lane reads: no LDS traffic.
 // Every lane of a row of 16 ends with the row's sum after four steps (xor 1,

@@ -41,8 +41,8 @@
  * M = 3 or 4 on matrices of more than 5120 rows) the levels are f16 and each
  * 32-value activation block is scaled by a power of two into f16 where that is
  * exact (every non-zero value of the block within 2^28 of its largest in
- * binary exponent); a wavefront whose blocks are not all exact in f16 computes
- * every weight as f16 level x fp32 scale (exact) times the bf16 activation in
+ * binary exponent, and the largest at least 2^-98); the blocks that are not
+ * are computed as f16 level x fp32 scale (exact) times the bf16 activation in
  * fp32 instead.  On the MFMA kernels (every other M, and nf4_gemm_prefill) the
  * levels are split into bf16 hi + lo and the bf16 activations are used as they
  * are.  Per output element
