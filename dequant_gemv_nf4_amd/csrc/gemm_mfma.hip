@@ -441,10 +441,15 @@ __global__ void __launch_bounds__(kThreads)
   if (S == 1) return;
   // K-splits: the last split of this tile group to finish adds all S partial
   // tiles in split order (the same bits whichever finishes last) and re-arms the
-  // group's counter for the next call.  Partials are written and read with
-  // agent-coherent accesses, so no cache of any XCD has to be written back or
-  // dropped; the stores are complete (vmcnt 0) before the counter moves, and the
-  // reads are issued only by the workgroup that saw the final count.
+  // group's counter for the next call.  Ordering (the AMDGPU memory model's
+  // release/acquire sequences, restricted to the locations involved): partials
+  // are written with agent-scope atomic stores, performed at the agent's
+  // coherence point and not held in one XCD's L2, so publishing them needs no L2
+  // write-back; vmcnt(0) waits until each thread's stores are performed, and
+  // the barrier orders those waits before the counter increment.  Only the
+  // workgroup that saw the final count reads them, with agent-scope atomic
+  // loads that also go to the coherence point (no stale L2 line can answer, so
+  // no invalidate is needed), issued after the increment returned.
   __shared__ int last;
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's partial stores are done
   __syncthreads();

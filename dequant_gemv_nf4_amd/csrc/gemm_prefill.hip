@@ -31,7 +31,10 @@
 // scales) in flight; the activation stage is double-buffered in LDS, one
 // barrier a step.  At the end the splits' tiles are added in split order.
 // Rows past M and columns past N re-read the last valid row or column and are
-// never stored.  No atomics, no cross-workgroup traffic: bitwise reproducible.
+// never stored.  Without a workspace there is no cross-workgroup traffic; with
+// one (nf4_gemm_prefill_ws) K is also split over workgroups whose partial tiles
+// meet in the workspace and are added in split order by the last to finish (the
+// end of the kernel).  Either way the results are bitwise reproducible.
 #include <utility>
 
 #include "nf4_device.h"
@@ -345,6 +348,15 @@ __global__ void __launch_bounds__(kPThreads * KS)
         }
       }
   }
+  // Ordering (the AMDGPU memory model's release/acquire sequences, restricted to
+  // the locations involved): every partial is written with an agent-scope
+  // atomic store, which is performed at the agent's coherence point rather than
+  // in one XCD's L2, so no L2 write-back is needed to publish it; vmcnt(0)
+  // waits until this thread's stores are performed there, and the barrier
+  // orders every thread's wait before the counter increment.  The workgroup that
+  // sees the final count reads the partials with agent-scope atomic loads, which
+  // also go to the coherence point (no stale L2 line can answer them, so no L2
+  // invalidate is needed), and it issues them only after the increment returned.
   __shared__ int last;
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores are done
   __syncthreads();
