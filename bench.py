@@ -683,7 +683,7 @@ def bench_layer_set(args, torch, dev):
                                                            for p in dom["projs"]])), 3),
                  "us_per_launch_p90": round(float(np.mean([per_proj[p]["us_p90"]
                                                            for p in dom["projs"]])), 3)})
-    if probe_out:
+    if probe_out and roof["bound"] == "hbm":
         probe_us = float(np.mean([per_proj[p]["probe_us"] for p in dom["projs"]]))
         roof["probe_us_per_launch"] = round(probe_us, 3)
         roof["pct_of_probe"] = round(100.0 * probe_us / us_launch, 2)

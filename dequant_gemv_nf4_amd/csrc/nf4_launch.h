@@ -34,7 +34,7 @@ inline bool use_valu(int64_t N, int64_t K, int M) {
 constexpr int kSplitCounters = 1024;
 constexpr int kSplitCounterBytes = kSplitCounters * 4;
 
-// MFMA product, 8 <= M <= 32.  With a workspace (workspace_bytes at least
+// MFMA product, 1 <= M <= 32.  With a workspace (workspace_bytes at least
 // gemm_mfma_workspace_bytes, its counter area zero before first use), K may be
 // split over workgroups; without one (nullptr), never.
 hipError_t launch_gemm_mfma(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,

@@ -3,6 +3,7 @@
     python rocpd_summary.py trace  <results.db> [name-filter] [prev]
     python rocpd_summary.py pmc    <results.db> [name-filter] [prev]
     python rocpd_summary.py copies <results.db> [name-filter]
+    python rocpd_summary.py total  <results.db> <name-filter> [...]
 
 `trace` groups dispatches by (kernel, grid, workgroup) and prints count, mean,
 median, p10 and p90 duration.  `pmc` prints the mean of every collected counter
@@ -11,8 +12,11 @@ kernel dispatched just before (labelled "after <kernel>"): two shapes that
 share a kernel and a grid but follow different launches come apart.  `copies` groups memory copies by direction and size (count,
 mean duration, GB/s), then reports how the copies and the filtered kernels
 overlap in time: the busy time of the copy engine over the span from the first
-to the last copy, and how many kernels ran while a copy was in flight.  All
-read only what rocprofv3 wrote.
+to the last copy, and how many kernels ran while a copy was in flight.
+`total` prints, for each filter, the count and mean duration of every dispatch
+whose full kernel name contains it (all grids together): the figure to hold
+against a bench line's per-launch mean when the projections it averages are
+dispatched in equal numbers.  All read only what rocprofv3 wrote.
 """
 import collections
 import sqlite3
@@ -21,7 +25,8 @@ import sys
 
 
 def _short(name: str) -> str:
-    return name.split("(")[0].replace("void ", "")
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0]
 
 
 def trace(path, filt="", by_prev=False):
@@ -66,6 +71,18 @@ def pmc(path, filt="", by_prev=False):
     return out
 
 
+def total(path, filters):
+    db = sqlite3.connect(path)
+    rows = db.execute("select name, start, end from kernels").fetchall()
+    out = []
+    for filt in filters:
+        d = sorted((e - s) / 1e3 for name, s, e in rows if filt in name)
+        if d:
+            out.append(f"{filt!r:40s} n {len(d):5d} mean {statistics.mean(d):9.3f} us  "
+                       f"median {statistics.median(d):9.3f}")
+    return out
+
+
 def copies(path, filt=""):
     db = sqlite3.connect(path)
     rows = db.execute("select name, size, start, end from memory_copies order by start").fetchall()
@@ -105,6 +122,8 @@ if __name__ == "__main__":
     filt = sys.argv[3] if len(sys.argv) > 3 else ""
     if mode == "copies":
         print("\n".join(copies(path, filt)))
+    elif mode == "total":
+        print("\n".join(total(path, sys.argv[3:])))
     else:
         by_prev = len(sys.argv) > 4 and sys.argv[4] == "prev"
         print("\n".join({"trace": trace, "pmc": pmc}[mode](path, filt, by_prev)))

@@ -155,3 +155,6 @@ def test_rocpd_summary_splits_by_preceding_kernel(tmp_path):
     pm = rs.pmc(str(tmp_path / "r.db"), "B", True)
     assert any("after A" in l and "X=3.0" in l for l in pm)
     assert any("after C" in l and "X=5.0" in l for l in pm)
+    tot = rs.total(str(tmp_path / "r.db"), ["B(", "A("])
+    assert " n     6 mean     4.000" in tot[0] and " n     3 mean    10.000" in tot[1]
+    assert rs._short("void (anonymous namespace)::probe_kernel<2>(int*)") == "probe_kernel<2>"
