@@ -396,7 +396,12 @@ __global__ void __launch_bounds__(kThreads)
         [&](auto slot) __attribute__((always_inline)) {
           constexpr int d = decltype(slot)::value;
           compute(slot);
-          load(slot, base + d + D);
+          // with one pair in flight and up to two tiles, no refill after the
+          // wave's last pair: the spare load would hold the wave at its end for
+          // one more memory round trip, and the wait before each pair is for
+          // every load in flight anyway (with more tiles the branch costs
+          // registers: spills at 7 tiles of two row tiles)
+          if (D > 1 || TB > 2 || base + d + D < nsteps) load(slot, base + d + D);
           // keep each slot's refill right after its use (the scheduler would
           // otherwise sink all refills to the end of the round)
           __builtin_amdgcn_sched_barrier(0);
@@ -626,10 +631,16 @@ __global__ void __launch_bounds__(kThreads)
   __builtin_amdgcn_sched_barrier(0);
   build_split_lut(lds, lane, wave);
   __syncthreads();
-  // one step in flight per wave: the refill follows the step's use
+  // one step in flight per wave: the refill follows the step's use.  Up to two
+  // tiles, no load goes out after the wave's last step: a spare load would still
+  // be waited for before the reduction (one more memory round trip; o 4096 x
+  // 4096 at M = 8: 7.2 -> 6.2 us without it).  The wait before each step is for
+  // every load in flight either way, so the branch costs no overlap.  (At 3 and
+  // 4 tiles the branch raises the register count past two workgroups per CU;
+  // those shapes, K above 8192 with more than 512 tiles, keep the spare load.)
   for (int i = 0; i < wn; ++i) {
     compute();
-    load(i + 1);
+    if (TB > 2 || i + 1 < wn) load(i + 1);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -649,6 +660,192 @@ __global__ void __launch_bounds__(kThreads)
     const int m = 4 * (ln >> 4) + rr;
     const int n = 16 * (t0 + j) + (ln & 15);
     if (t0 + j < NT && m < M && n < N) Y[(int64_t)m * N + n] = sum;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Streaming form of the quad step for M <= 8 and more column tiles than CUs
+// (gemm_mfma_stream_kernel).  One workgroup of 8 waves per CU walks IT tiles,
+// tile t*nblocks + b, so the whole grid streams one band of rows at a time.  A
+// wave owns the same steps of K, [q0, q0 + ns), in every tile: its activation
+// fragments (both halves) are loaded once and stay in registers, instead of
+// being read again from L2 for every tile, and the code and scale loads of two
+// tiles are in flight per wave.  Each tile has its own accumulator; after the
+// last tile the eight partials of a tile are added in LDS in slice order
+// (deterministic, and the same sums in the same order as the quad-step
+// kernel, so both give identical bits).  The slices are rotated by the
+// workgroup index so that the CUs do not all read the same activation lines at
+// the same moment (q|k|v 6144 x 4096 at M = 8: 10.2 -> 9.4 us).  Llama-3.1-8B
+// gate|up (28672 x 4096) at M = 8: 26.0 -> 19 us against the quad step.
+// ---------------------------------------------------------------------------
+template <int NS, int IT>
+__global__ void __launch_bounds__(kThreads)
+    gemm_mfma_stream_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
+                            const uint16_t *__restrict__ X, float *__restrict__ Y, int N, int K,
+                            int M, int nblocks) {
+  static_assert(kWaves * IT * 256 <= kLutWords, "the partials reuse the table's LDS");
+  __shared__ __attribute__((aligned(16))) uint32_t lds[kLutWords];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, lg = lane >> 4;
+  const bool upper = col >= 8;
+  const int m8 = col & 7;
+  const int NG = K >> 6;
+  const int NQ = NG >> 2;
+  const int NT = (N + 15) >> 4;
+  const int slice = (wave + (int)blockIdx.x) & (kWaves - 1);
+  const int q0 = slice * NQ / kWaves;
+  const int ns = (slice + 1) * NQ / kWaves - q0;  // 0 <= ns <= NS
+
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(codes), 0, (int)((int64_t)N * (K >> 1)), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(scales), 0, (int)((int64_t)N * NG * 2), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(X), 0, M * K * 2, kBufferWord3);
+
+  // per-lane offsets within a tile starting at row 0 (the quad step's chunk
+  // assignment); the tile's row offset and the step's offset are scalars
+  const int cv0 = m8 * (K >> 1) + 16 * (lg + (upper ? 4 : 0));
+  const int cv1 = (8 + m8) * (K >> 1) + 16 * (lg + (upper ? 0 : 4));
+  const int svo = col * NG * 2;
+  const int xvo = (min(m8, M - 1) * K) * 2 + 64 * (lg & 1) + 32 * (lg >> 1) + (upper ? 16 : 0);
+
+  // step of register slot s (slots past the slice re-read its last step)
+  auto step_of = [&](int s) {
+    return __builtin_amdgcn_readfirstlane(max(min(q0 + min(s, ns - 1), NQ - 1), 0));
+  };
+  // first row of tile t of this workgroup: a last, partial tile is moved back to
+  // end at row N - 1 (its rows below 16 * tile belong to the tile before and are
+  // not stored), and tiles past the end re-read the last one
+  auto tile_row = [&](int t) {
+    const int tile = min(t * nblocks + (int)blockIdx.x, NT - 1);
+    return __builtin_amdgcn_readfirstlane(min(16 * tile, N - 16));
+  };
+
+  u32x4_t A[NS][4][2];  // [step][group][half]
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int q = step_of(s);
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq)
+      A[s][gq][0] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xvo + 128 * gq, 512 * q, 0);
+  }
+
+  constexpr int kRing = IT < 2 ? IT : 2;  // tiles in flight
+  u32x4_t rc[kRing][NS][2];
+  u32x2_t rs[kRing][NS];
+  auto load_tile = [&](auto slot, int t) __attribute__((always_inline)) {
+    constexpr int d = decltype(slot)::value;
+    const int tb = tile_row(t);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int q = step_of(s);
+      const int coff = tb * (K >> 1) + 128 * q;
+      rc[d][s][0] = __builtin_amdgcn_raw_buffer_load_b128(crs, cv0, coff, kLoadStream);
+      rc[d][s][1] = __builtin_amdgcn_raw_buffer_load_b128(crs, cv1, coff, kLoadStream);
+      rs[d][s] = __builtin_amdgcn_raw_buffer_load_b64(srs, svo, tb * NG * 2 + 8 * q, 0);
+    }
+  };
+
+  f32x4_t acc[IT];
+#pragma unroll
+  for (int t = 0; t < IT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const uint32_t laneoff = 8u * (lane & 31);
+  auto compute = [&](auto slot, f32x4_t &ac) __attribute__((always_inline)) {
+    constexpr int d = decltype(slot)::value;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (s >= ns) break;
+      // the quad step's exchange: own chunk and the partner's, then lane-groups
+      // g and g + 2 trade words so that words 2q, 2q + 1 hold group q
+      uint32_t r[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t own = upper ? rc[d][s][1][e] : rc[d][s][0][e];
+        const uint32_t out = upper ? rc[d][s][0][e] : rc[d][s][1][e];
+        r[e] = own;
+        r[4 + e] = (uint32_t)__builtin_amdgcn_mov_dpp((int)out, 0x128, 0xf, 0xf, false);
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const auto lo = __builtin_amdgcn_permlane32_swap(r[e], r[2 + e], false, false);
+        r[e] = lo[0];
+        r[2 + e] = lo[1];
+        const auto hi = __builtin_amdgcn_permlane32_swap(r[4 + e], r[6 + e], false, false);
+        r[4 + e] = hi[0];
+        r[6 + e] = hi[1];
+      }
+      const u32x2_t sw = rs[d][s];
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        f32x4_t g;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t w = r[2 * gq + h];
+          u32x4_t bh, bl;
+          u32x2_t e;
+          e = lds_load_u64(lds, split_addr<0>(w, laneoff)); bh[0] = e[0]; bl[0] = e[1];
+          e = lds_load_u64(lds, split_addr<1>(w, laneoff)); bh[1] = e[0]; bl[1] = e[1];
+          e = lds_load_u64(lds, split_addr<2>(w, laneoff)); bh[2] = e[0]; bl[2] = e[1];
+          e = lds_load_u64(lds, split_addr<3>(w, laneoff)); bh[3] = e[0]; bl[3] = e[1];
+          g = mfma_bf16(A[s][gq][h], bh, h == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : g);
+          g = mfma_bf16(A[s][gq][h], bl, g);
+        }
+        const uint32_t sword = sw[gq >> 1];
+        const float sc = f16_bits_to_f32((gq & 1) ? (sword >> 16) : (sword & 0xffffu));
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) ac[rr] = fmaf(g[rr], sc, ac[rr]);
+      }
+    }
+  };
+
+  load_tile(Slot<0>{}, 0);
+  if constexpr (IT > 1) load_tile(Slot<1>{}, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  build_split_lut(lds, lane, wave);
+  // the partner half of each activation fragment: lane n +- 8 of the row
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        A[s][gq][1][e] =
+            (uint32_t)__builtin_amdgcn_mov_dpp((int)A[s][gq][0][e], 0x128, 0xf, 0xf, false);
+  __syncthreads();
+  // tiles unrolled, so the ring slots are compile-time registers and no load
+  // goes out past the last tile
+  [&]<int... t>(std::integer_sequence<int, t...>) {
+    (
+        [&] {
+          compute(Slot<t % kRing>{}, acc[t]);
+          if constexpr (t + kRing < IT) load_tile(Slot<t % kRing>{}, t + kRing);
+          __builtin_amdgcn_sched_barrier(0);
+        }(),
+        ...);
+  }(std::make_integer_sequence<int, IT>{});
+
+  __syncthreads();  // the table is no longer read
+  float *red = reinterpret_cast<float *>(lds);
+#pragma unroll
+  for (int t = 0; t < IT; ++t)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) red[((slice * IT + t) * 4 + rr) * 64 + lane] = acc[t][rr];
+  __syncthreads();
+  constexpr int kOut = IT * 256;
+  for (int o = tid; o < kOut; o += kThreads) {
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) sum += red[w * kOut + o];
+    const int ln = o & 63, rr = (o >> 6) & 3, t = o >> 8;
+    const int tile = t * nblocks + (int)blockIdx.x;
+    const int m = 4 * (ln >> 4) + rr;
+    const int n = min(16 * tile, N - 16) + (ln & 15);
+    if (tile < NT && m < M && n >= 16 * tile && n < N) Y[(int64_t)m * N + n] = sum;
   }
 }
 
@@ -722,6 +919,54 @@ hipError_t go_quad_plan(const uint8_t *codes, const uint16_t *scales, int N, int
   }
 }
 
+template <int NS, int IT>
+hipError_t go_stream(const uint8_t *codes, const uint16_t *scales, int N, int K, const uint16_t *X,
+                     int M, float *Y, int nblocks, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_mfma_stream_kernel<NS, IT>), dim3(nblocks), dim3(kThreads), 0, stream,
+                     codes, scales, X, Y, N, K, M, nblocks);
+  return hipGetLastError();
+}
+
+template <int NS>
+hipError_t go_stream_it(int it, const uint8_t *codes, const uint16_t *scales, int N, int K,
+                        const uint16_t *X, int M, float *Y, int nb, hipStream_t s) {
+  switch (it) {
+    case 2: return go_stream<NS, 2>(codes, scales, N, K, X, M, Y, nb, s);
+    case 3: return go_stream<NS, 3>(codes, scales, N, K, X, M, Y, nb, s);
+    case 4: return go_stream<NS, 4>(codes, scales, N, K, X, M, Y, nb, s);
+    case 5: return go_stream<NS, 5>(codes, scales, N, K, X, M, Y, nb, s);
+    case 6: return go_stream<NS, 6>(codes, scales, N, K, X, M, Y, nb, s);
+    case 7: return go_stream<NS, 7>(codes, scales, N, K, X, M, Y, nb, s);
+    default: return go_stream<NS, 8>(codes, scales, N, K, X, M, Y, nb, s);
+  }
+}
+
+// Streaming plan: one workgroup per CU, 2 to 8 tiles each, at most 4 steps per
+// wave (the activation fragments of 4 steps are 128 registers).  Measured
+// against the quad step on the Llama-3.1-8B shapes: ahead wherever a workgroup
+// gets two or more tiles; at one tile per CU (4096 columns) the quad step is as
+// fast or faster, and with 7 steps per wave (down, 14336 of K) all steps in
+// flight ran slower (17.9 vs 14.1 us).
+bool stream_plan(int N, int K, int &ns, int &it, int &nb) {
+  const int NQ = (K >> 6) >> 2;
+  const int tiles = (N + 15) / 16;
+  ns = (NQ + kWaves - 1) / kWaves;
+  nb = std::min(tiles, kCUs);
+  it = (tiles + nb - 1) / nb;
+  return tiles > kCUs && ns >= 1 && ns <= 4 && it <= 8;
+}
+
+hipError_t go_stream_plan(const uint8_t *codes, const uint16_t *scales, int N, int K,
+                          const uint16_t *X, int M, float *Y, int ns, int it, int nb,
+                          hipStream_t s) {
+  switch (ns) {
+    case 1: return go_stream_it<1>(it, codes, scales, N, K, X, M, Y, nb, s);
+    case 2: return go_stream_it<2>(it, codes, scales, N, K, X, M, Y, nb, s);
+    case 3: return go_stream_it<3>(it, codes, scales, N, K, X, M, Y, nb, s);
+    default: return go_stream_it<4>(it, codes, scales, N, K, X, M, Y, nb, s);
+  }
+}
+
 // Pair-step plan: TB column tiles per workgroup and S K-splits.  Without a
 // workspace, S = 1 and TB just gives every CU a workgroup.  With one, K is split
 // where a sweep of (TB, S) over the Llama-3.1-8B shapes measured it faster:
@@ -780,6 +1025,11 @@ bool quad_shape(int K, int M) { return M <= 8 && (K >> 6) % 4 == 0; }
 
 }  // namespace
 
+bool gemm_mfma_streams(int64_t N, int64_t K, int M) {
+  int ns, it, nb;
+  return M >= 1 && quad_shape((int)K, M) && stream_plan((int)N, (int)K, ns, it, nb);
+}
+
 int64_t gemm_mfma_workspace_bytes(int64_t N, int64_t K, int M) {
   if (M < 1 || M > 32 || (K >> 6) % 2 != 0 || quad_shape((int)K, M)) return 0;
   return pair_workspace_bytes((int)N, M, plan_pair((int)N, (int)K, M, true));
@@ -792,8 +1042,12 @@ hipError_t launch_gemm_mfma(const uint8_t *codes, const uint16_t *scales, int64_
   const int n = (int)N, k = (int)K;
   // pair steps need an even group count and 4-byte aligned scales (every model
   // shape); otherwise one group per step
-  if (quad_shape(k, M) && (reinterpret_cast<uintptr_t>(scales) & 7) == 0)
+  if (quad_shape(k, M) && (reinterpret_cast<uintptr_t>(scales) & 7) == 0) {
+    int ns, it, nb;
+    if (stream_plan(n, k, ns, it, nb))
+      return go_stream_plan(codes, scales, n, k, X, M, Y, ns, it, nb, stream);
     return go_quad_plan(codes, scales, n, k, X, M, Y, stream);
+  }
   const bool pair = ((k >> 6) % 2 == 0) && ((reinterpret_cast<uintptr_t>(scales) & 3) == 0);
   if (pair) {
     PairPlan p = plan_pair(n, k, M, workspace != nullptr && !quad_shape(k, M));

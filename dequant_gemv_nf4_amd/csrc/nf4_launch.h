@@ -16,13 +16,20 @@ hipError_t launch_gemv_valu(const uint8_t *codes, const uint16_t *scales, int64_
                             const uint16_t *X, int M, float *Y, hipStream_t stream);
 bool valu_supported(int64_t N, int64_t K, int M);
 
+// Whether the MFMA product of this shape runs in the streaming form (several
+// column tiles per workgroup, activation fragments kept in registers).
+bool gemm_mfma_streams(int64_t N, int64_t K, int M);
+
 // Which kernel a batch of M rows runs on: the vector-ALU kernel (one weight
 // decode shared by M dot products) for M <= 2, and for M = 3 and 4 on matrices
-// of more than 5120 rows; the MFMA kernel otherwise.  Measured on the
-// Llama-3.1-8B shapes (graph replays): MFMA wins from M = 5 everywhere and at
-// M = 3 and 4 on 4096 rows (4096x4096 at M = 4: 6.5 vs 7.1 us); VALU at M = 3
-// and 4 on 6144 rows (M = 4: 8.2 vs 9.2 us) and 28672 rows (M = 4: 21.0 vs 27.9).
+// of more than 5120 rows, except M = 4 above 16384 rows where the streaming
+// MFMA form takes it; the MFMA kernel otherwise.  Measured on the Llama-3.1-8B
+// shapes (graph replays): MFMA wins from M = 5 everywhere and at M = 3 and 4 on
+// 4096 rows (4096x4096 at M = 4: 5.5 vs 7.1 us); VALU at M = 3 and 4 on 6144
+// rows (M = 4: 8.6 vs 8.9 us) and at M = 3 on 28672 rows (18.4 vs 18.9); the
+// streaming MFMA form at M = 4 on 28672 rows (18.2 vs 21.3).
 inline bool use_valu(int64_t N, int64_t K, int M) {
+  if (M == 4 && N > 16384 && gemm_mfma_streams(N, K, M)) return false;
   return (M <= 2 || (M <= 4 && N > 5120)) && valu_supported(N, K, M);
 }
 

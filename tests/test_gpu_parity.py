@@ -206,6 +206,18 @@ def test_gemm_quad_steps(nf4, M, N, K):
     _product_case(nf4, M, N, K, seed=4)
 
 
+@pytest.mark.parametrize("M,N,K", [(4, 16400, 1024), (8, 8200, 8192), (5, 4200, 5120),
+                                   (8, 32768, 256), (6, 32784, 512), (7, 4113, 2048)])
+def test_gemm_streaming_form(nf4, M, N, K):
+    """M <= 8 with more 16-column tiles than CUs runs the streaming form: M = 4
+    above 16384 rows (taken from the vector-ALU kernel), 4 steps per wave and 3
+    tiles per workgroup with a partial last tile, slices of 2 and 3 steps
+    (K = 5120), one step in all (K = 256: seven slices empty) with 8 tiles per
+    workgroup, 9 tiles per workgroup (past the form's limit: quad steps), and a
+    last tile of one row."""
+    _product_case(nf4, M, N, K, seed=5)
+
+
 def test_gemm_quad_shape_with_scales_only_4_byte_aligned(nf4):
     """Scales 4 but not 8 bytes aligned: the quad-step shape falls back to the
     pair-step kernel, without a K-split (no workspace is planned for it)."""
