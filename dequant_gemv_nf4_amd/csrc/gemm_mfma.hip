@@ -664,8 +664,10 @@ __global__ void __launch_bounds__(kThreads)
 }
 
 // ---------------------------------------------------------------------------
-// Streaming form of the quad step for M <= 8 and more column tiles than CUs
-// (gemm_mfma_stream_kernel).  One workgroup of 8 waves per CU walks IT tiles,
+// Streaming form of the quad step for more column tiles than CUs, M <= 32
+// (gemm_mfma_stream_kernel).  MR = 8 (M <= 8) keeps the quad step's activation
+// loads (rows 8..15 of the tile are padding); MR = 16 and 32 load one or two
+// full 16-row activation tiles, both halves of each fragment.  One workgroup of 8 waves per CU walks IT tiles,
 // tile t*nblocks + b, so the whole grid streams one band of rows at a time.  A
 // wave owns the same steps of K, [q0, q0 + ns), in every tile: its activation
 // fragments (both halves) are loaded once and stay in registers, instead of
@@ -678,13 +680,17 @@ __global__ void __launch_bounds__(kThreads)
 // the same moment (q|k|v 6144 x 4096 at M = 8: 10.2 -> 9.4 us).  Llama-3.1-8B
 // gate|up (28672 x 4096) at M = 8: 26.0 -> 19 us against the quad step.
 // ---------------------------------------------------------------------------
-template <int NS, int IT>
+template <int MR, int NS, int IT>
 __global__ void __launch_bounds__(kThreads)
     gemm_mfma_stream_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
                             const uint16_t *__restrict__ X, float *__restrict__ Y, int N, int K,
                             int M, int nblocks) {
-  static_assert(kWaves * IT * 256 <= kLutWords, "the partials reuse the table's LDS");
-  __shared__ __attribute__((aligned(16))) uint32_t lds[kLutWords];
+  // MR = 8: rows 8..15 of the 16-row tile are padding (the quad step's
+  // activation loads); MR = 16 or 32: one or two full 16-row tiles
+  constexpr int MT = MR == 32 ? 2 : 1;
+  constexpr int kRedWords = kWaves * IT * MT * 256;
+  constexpr int kLdsWords = kRedWords > kLutWords ? kRedWords : kLutWords;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsWords];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -711,7 +717,13 @@ __global__ void __launch_bounds__(kThreads)
   const int cv0 = m8 * (K >> 1) + 16 * (lg + (upper ? 4 : 0));
   const int cv1 = (8 + m8) * (K >> 1) + 16 * (lg + (upper ? 0 : 4));
   const int svo = col * NG * 2;
-  const int xvo = (min(m8, M - 1) * K) * 2 + 64 * (lg & 1) + 32 * (lg >> 1) + (upper ? 16 : 0);
+  // activations of lane-group g in group q of a step: k = 64 q + 32 (g & 1) +
+  // 16 (g >> 1) + 8 h + e, the offsets the exchange leaves the weights at
+  int xvo[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    xvo[mt] = MR == 8 ? (min(m8, M - 1) * K) * 2 + 64 * (lg & 1) + 32 * (lg >> 1) + (upper ? 16 : 0)
+                      : (min(16 * mt + col, M - 1) * K) * 2 + 64 * (lg & 1) + 32 * (lg >> 1);
 
   // step of register slot s (slots past the slice re-read its last step)
   auto step_of = [&](int s) {
@@ -725,13 +737,18 @@ __global__ void __launch_bounds__(kThreads)
     return __builtin_amdgcn_readfirstlane(min(16 * tile, N - 16));
   };
 
-  u32x4_t A[NS][4][2];  // [step][group][half]
+  u32x4_t A[NS][MT][4][2];  // [step][row tile][group][half]
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int q = step_of(s);
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq)
-      A[s][gq][0] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xvo + 128 * gq, 512 * q, 0);
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+        for (int h = 0; h < (MR == 8 ? 1 : 2); ++h)
+          A[s][mt][gq][h] =
+              __builtin_amdgcn_raw_buffer_load_b128(xrs, xvo[mt] + 128 * gq + 16 * h, 512 * q, 0);
   }
 
   constexpr int kRing = IT < 2 ? IT : 2;  // tiles in flight
@@ -750,12 +767,14 @@ __global__ void __launch_bounds__(kThreads)
     }
   };
 
-  f32x4_t acc[IT];
+  f32x4_t acc[IT][MT];
 #pragma unroll
-  for (int t = 0; t < IT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < IT; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const uint32_t laneoff = 8u * (lane & 31);
-  auto compute = [&](auto slot, f32x4_t &ac) __attribute__((always_inline)) {
+  auto compute = [&](auto slot, f32x4_t (&ac)[MT]) __attribute__((always_inline)) {
     constexpr int d = decltype(slot)::value;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -782,7 +801,7 @@ __global__ void __launch_bounds__(kThreads)
       const u32x2_t sw = rs[d][s];
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        f32x4_t g;
+        f32x4_t g[MT];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const uint32_t w = r[2 * gq + h];
@@ -792,13 +811,18 @@ __global__ void __launch_bounds__(kThreads)
           e = lds_load_u64(lds, split_addr<1>(w, laneoff)); bh[1] = e[0]; bl[1] = e[1];
           e = lds_load_u64(lds, split_addr<2>(w, laneoff)); bh[2] = e[0]; bl[2] = e[1];
           e = lds_load_u64(lds, split_addr<3>(w, laneoff)); bh[3] = e[0]; bl[3] = e[1];
-          g = mfma_bf16(A[s][gq][h], bh, h == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : g);
-          g = mfma_bf16(A[s][gq][h], bl, g);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            g[mt] = mfma_bf16(A[s][mt][gq][h], bh, h == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : g[mt]);
+            g[mt] = mfma_bf16(A[s][mt][gq][h], bl, g[mt]);
+          }
         }
         const uint32_t sword = sw[gq >> 1];
         const float sc = f16_bits_to_f32((gq & 1) ? (sword >> 16) : (sword & 0xffffu));
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) ac[rr] = fmaf(g[rr], sc, ac[rr]);
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) ac[mt][rr] = fmaf(g[mt][rr], sc, ac[mt][rr]);
       }
     }
   };
@@ -807,15 +831,18 @@ __global__ void __launch_bounds__(kThreads)
   if constexpr (IT > 1) load_tile(Slot<1>{}, 1);
   __builtin_amdgcn_sched_barrier(0);
   build_split_lut(lds, lane, wave);
-  // the partner half of each activation fragment: lane n +- 8 of the row
+  // MR = 8: the second half of each activation fragment comes from lane n +- 8
+  // of the row, which loaded it (a DPP row rotation by 8)
+  if constexpr (MR == 8) {
 #pragma unroll
-  for (int s = 0; s < NS; ++s)
+    for (int s = 0; s < NS; ++s)
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq)
+      for (int gq = 0; gq < 4; ++gq)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        A[s][gq][1][e] =
-            (uint32_t)__builtin_amdgcn_mov_dpp((int)A[s][gq][0][e], 0x128, 0xf, 0xf, false);
+        for (int e = 0; e < 4; ++e)
+          A[s][0][gq][1][e] =
+              (uint32_t)__builtin_amdgcn_mov_dpp((int)A[s][0][gq][0][e], 0x128, 0xf, 0xf, false);
+  }
   __syncthreads();
   // tiles unrolled, so the ring slots are compile-time registers and no load
   // goes out past the last tile
@@ -834,16 +861,20 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
   for (int t = 0; t < IT; ++t)
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) red[((slice * IT + t) * 4 + rr) * 64 + lane] = acc[t][rr];
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        red[(((slice * IT + t) * MT + mt) * 4 + rr) * 64 + lane] = acc[t][mt][rr];
   __syncthreads();
-  constexpr int kOut = IT * 256;
+  constexpr int kOut = IT * MT * 256;
   for (int o = tid; o < kOut; o += kThreads) {
     float sum = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) sum += red[w * kOut + o];
-    const int ln = o & 63, rr = (o >> 6) & 3, t = o >> 8;
+    const int ln = o & 63, rr = (o >> 6) & 3, tm = o >> 8;
+    const int t = tm / MT, mt = tm % MT;
     const int tile = t * nblocks + (int)blockIdx.x;
-    const int m = 4 * (ln >> 4) + rr;
+    const int m = 16 * mt + 4 * (ln >> 4) + rr;
     const int n = min(16 * tile, N - 16) + (ln & 15);
     if (tile < NT && m < M && n >= 16 * tile && n < N) Y[(int64_t)m * N + n] = sum;
   }
@@ -919,52 +950,64 @@ hipError_t go_quad_plan(const uint8_t *codes, const uint16_t *scales, int N, int
   }
 }
 
-template <int NS, int IT>
+template <int MR, int NS, int IT>
 hipError_t go_stream(const uint8_t *codes, const uint16_t *scales, int N, int K, const uint16_t *X,
                      int M, float *Y, int nblocks, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_mfma_stream_kernel<NS, IT>), dim3(nblocks), dim3(kThreads), 0, stream,
-                     codes, scales, X, Y, N, K, M, nblocks);
+  hipLaunchKernelGGL((gemm_mfma_stream_kernel<MR, NS, IT>), dim3(nblocks), dim3(kThreads), 0,
+                     stream, codes, scales, X, Y, N, K, M, nblocks);
   return hipGetLastError();
 }
 
-template <int NS>
+template <int MR, int NS>
 hipError_t go_stream_it(int it, const uint8_t *codes, const uint16_t *scales, int N, int K,
                         const uint16_t *X, int M, float *Y, int nb, hipStream_t s) {
   switch (it) {
-    case 2: return go_stream<NS, 2>(codes, scales, N, K, X, M, Y, nb, s);
-    case 3: return go_stream<NS, 3>(codes, scales, N, K, X, M, Y, nb, s);
-    case 4: return go_stream<NS, 4>(codes, scales, N, K, X, M, Y, nb, s);
-    case 5: return go_stream<NS, 5>(codes, scales, N, K, X, M, Y, nb, s);
-    case 6: return go_stream<NS, 6>(codes, scales, N, K, X, M, Y, nb, s);
-    case 7: return go_stream<NS, 7>(codes, scales, N, K, X, M, Y, nb, s);
-    default: return go_stream<NS, 8>(codes, scales, N, K, X, M, Y, nb, s);
+    case 2: return go_stream<MR, NS, 2>(codes, scales, N, K, X, M, Y, nb, s);
+    case 3: return go_stream<MR, NS, 3>(codes, scales, N, K, X, M, Y, nb, s);
+    case 4: return go_stream<MR, NS, 4>(codes, scales, N, K, X, M, Y, nb, s);
+    case 5: return go_stream<MR, NS, 5>(codes, scales, N, K, X, M, Y, nb, s);
+    case 6: return go_stream<MR, NS, 6>(codes, scales, N, K, X, M, Y, nb, s);
+    case 7: return go_stream<MR, NS, 7>(codes, scales, N, K, X, M, Y, nb, s);
+    default: return go_stream<MR, NS, 8>(codes, scales, N, K, X, M, Y, nb, s);
   }
 }
 
-// Streaming plan: one workgroup per CU, 2 to 8 tiles each, at most 4 steps per
-// wave (the activation fragments of 4 steps are 128 registers).  Measured
-// against the quad step on the Llama-3.1-8B shapes: ahead wherever a workgroup
-// gets two or more tiles; at one tile per CU (4096 columns) the quad step is as
-// fast or faster, and with 7 steps per wave (down, 14336 of K) all steps in
-// flight ran slower (17.9 vs 14.1 us).
-bool stream_plan(int N, int K, int &ns, int &it, int &nb) {
+// Streaming plan: one workgroup per CU, 2 to 8 tiles each (3 to 8 above M = 8),
+// at most 4 steps per wave at M <= 8 (the activation fragments of 4 steps are
+// 128 registers), 2 at M = 9..32.  Measured on the Llama-3.1-8B shapes: ahead
+// of the quad step wherever a workgroup gets two or more tiles; at one tile per
+// CU (4096 columns) the quad step is as fast or faster, and with 7 steps per
+// wave (down, 14336 of K) all steps in flight ran slower (17.9 vs 14.1 us).
+// Against the pair step (M = 9..32): gate|up 28672 x 4096 at M = 12, 16, 32
+// 29.6, 30.3, 35.6 -> 19.5, 20.0, 26.0 us; at two tiles per CU (q|k|v, 6144
+// rows) even or behind (M = 32: 14.8 vs 14.5), so from three.
+bool stream_plan(int N, int K, int M, int &ns, int &it, int &nb) {
   const int NQ = (K >> 6) >> 2;
   const int tiles = (N + 15) / 16;
   ns = (NQ + kWaves - 1) / kWaves;
   nb = std::min(tiles, kCUs);
   it = (tiles + nb - 1) / nb;
-  return tiles > kCUs && ns >= 1 && ns <= 4 && it <= 8;
+  return M >= 1 && M <= 32 && (K >> 6) % 4 == 0 && tiles > kCUs && ns >= 1 &&
+         ns <= (M <= 8 ? 4 : 2) && it >= (M <= 8 ? 2 : 3) && it <= 8;
+}
+
+template <int MR>
+hipError_t go_stream_ns(int ns, int it, const uint8_t *codes, const uint16_t *scales, int N,
+                        int K, const uint16_t *X, int M, float *Y, int nb, hipStream_t s) {
+  switch (ns) {
+    case 1: return go_stream_it<MR, 1>(it, codes, scales, N, K, X, M, Y, nb, s);
+    case 2: return go_stream_it<MR, 2>(it, codes, scales, N, K, X, M, Y, nb, s);
+    case 3: return go_stream_it<MR, MR == 8 ? 3 : 2>(it, codes, scales, N, K, X, M, Y, nb, s);
+    default: return go_stream_it<MR, MR == 8 ? 4 : 2>(it, codes, scales, N, K, X, M, Y, nb, s);
+  }
 }
 
 hipError_t go_stream_plan(const uint8_t *codes, const uint16_t *scales, int N, int K,
                           const uint16_t *X, int M, float *Y, int ns, int it, int nb,
                           hipStream_t s) {
-  switch (ns) {
-    case 1: return go_stream_it<1>(it, codes, scales, N, K, X, M, Y, nb, s);
-    case 2: return go_stream_it<2>(it, codes, scales, N, K, X, M, Y, nb, s);
-    case 3: return go_stream_it<3>(it, codes, scales, N, K, X, M, Y, nb, s);
-    default: return go_stream_it<4>(it, codes, scales, N, K, X, M, Y, nb, s);
-  }
+  if (M <= 8) return go_stream_ns<8>(ns, it, codes, scales, N, K, X, M, Y, nb, s);
+  if (M <= 16) return go_stream_ns<16>(ns, it, codes, scales, N, K, X, M, Y, nb, s);
+  return go_stream_ns<32>(ns, it, codes, scales, N, K, X, M, Y, nb, s);
 }
 
 // Pair-step plan: TB column tiles per workgroup and S K-splits.  Without a
@@ -1027,7 +1070,7 @@ bool quad_shape(int K, int M) { return M <= 8 && (K >> 6) % 4 == 0; }
 
 bool gemm_mfma_streams(int64_t N, int64_t K, int M) {
   int ns, it, nb;
-  return M >= 1 && quad_shape((int)K, M) && stream_plan((int)N, (int)K, ns, it, nb);
+  return stream_plan((int)N, (int)K, M, ns, it, nb);
 }
 
 int64_t gemm_mfma_workspace_bytes(int64_t N, int64_t K, int M) {
@@ -1042,12 +1085,11 @@ hipError_t launch_gemm_mfma(const uint8_t *codes, const uint16_t *scales, int64_
   const int n = (int)N, k = (int)K;
   // pair steps need an even group count and 4-byte aligned scales (every model
   // shape); otherwise one group per step
-  if (quad_shape(k, M) && (reinterpret_cast<uintptr_t>(scales) & 7) == 0) {
-    int ns, it, nb;
-    if (stream_plan(n, k, ns, it, nb))
-      return go_stream_plan(codes, scales, n, k, X, M, Y, ns, it, nb, stream);
-    return go_quad_plan(codes, scales, n, k, X, M, Y, stream);
-  }
+  const bool aligned8 = (reinterpret_cast<uintptr_t>(scales) & 7) == 0;
+  int ns, it, nb;
+  if (aligned8 && stream_plan(n, k, M, ns, it, nb))
+    return go_stream_plan(codes, scales, n, k, X, M, Y, ns, it, nb, stream);
+  if (quad_shape(k, M) && aligned8) return go_quad_plan(codes, scales, n, k, X, M, Y, stream);
   const bool pair = ((k >> 6) % 2 == 0) && ((reinterpret_cast<uintptr_t>(scales) & 3) == 0);
   if (pair) {
     PairPlan p = plan_pair(n, k, M, workspace != nullptr && !quad_shape(k, M));

@@ -207,14 +207,17 @@ def test_gemm_quad_steps(nf4, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(4, 16400, 1024), (8, 8200, 8192), (5, 4200, 5120),
-                                   (8, 32768, 256), (6, 32784, 512), (7, 4113, 2048)])
+                                   (8, 32768, 256), (6, 32784, 512), (7, 4113, 2048),
+                                   (9, 12296, 4096), (16, 20000, 1280), (17, 28672, 2048),
+                                   (32, 12290, 512), (24, 8200, 4096)])
 def test_gemm_streaming_form(nf4, M, N, K):
-    """M <= 8 with more 16-column tiles than CUs runs the streaming form: M = 4
-    above 16384 rows (taken from the vector-ALU kernel), 4 steps per wave and 3
-    tiles per workgroup with a partial last tile, slices of 2 and 3 steps
-    (K = 5120), one step in all (K = 256: seven slices empty) with 8 tiles per
-    workgroup, 9 tiles per workgroup (past the form's limit: quad steps), and a
-    last tile of one row."""
+    """More 16-column tiles than CUs run the streaming form: M = 4 above 16384
+    rows (taken from the vector-ALU kernel), 4 steps per wave and 3 tiles per
+    workgroup with a partial last tile, slices of 2 and 3 steps (K = 5120), one
+    step in all (K = 256: seven slices empty) with 8 tiles per workgroup, 9 tiles
+    per workgroup (past the form's limit: quad steps), a last tile of one row;
+    above M = 8 one full 16-row tile (M = 9, 16, with slices of 1 and 2 steps)
+    and two (M = 17, 24, 32), with partial last tiles of 8 and 2 rows."""
     _product_case(nf4, M, N, K, seed=5)
 
 
