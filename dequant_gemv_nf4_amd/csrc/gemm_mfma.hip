@@ -684,7 +684,7 @@ template <int MR, int NS, int IT>
 __global__ void __launch_bounds__(kThreads)
     gemm_mfma_stream_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
                             const uint16_t *__restrict__ X, float *__restrict__ Y, int N, int K,
-                            int M, int nblocks) {
+                            int M, int nblocks, int S, uint32_t *__restrict__ cnt) {
   // MR = 8: rows 8..15 of the 16-row tile are padding (the quad step's
   // activation loads); MR = 16 or 32: one or two full 16-row tiles
   constexpr int MT = MR == 32 ? 2 : 1;
@@ -701,9 +701,16 @@ __global__ void __launch_bounds__(kThreads)
   const int NG = K >> 6;
   const int NQ = NG >> 2;
   const int NT = (N + 15) >> 4;
+  // K-split blockIdx.y of S takes the steps [p0, p0 + np); its waves share them
+  const int split = blockIdx.y;
+  const int p0 = split * NQ / S;
+  const int np = (split + 1) * NQ / S - p0;
   const int slice = (wave + (int)blockIdx.x) & (kWaves - 1);
-  const int q0 = slice * NQ / kWaves;
-  const int ns = (slice + 1) * NQ / kWaves - q0;  // 0 <= ns <= NS
+  const int q0 = p0 + slice * np / kWaves;
+  const int ns = p0 + (slice + 1) * np / kWaves - q0;  // 0 <= ns <= NS
+  float *const part =
+      S > 1 ? reinterpret_cast<float *>(reinterpret_cast<char *>(cnt) + kSplitCounterBytes)
+            : nullptr;
 
   const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t *>(codes), 0, (int)((int64_t)N * (K >> 1)), kBufferWord3);
@@ -867,16 +874,48 @@ __global__ void __launch_bounds__(kThreads)
         red[(((slice * IT + t) * MT + mt) * 4 + rr) * 64 + lane] = acc[t][mt][rr];
   __syncthreads();
   constexpr int kOut = IT * MT * 256;
-  for (int o = tid; o < kOut; o += kThreads) {
-    float sum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) sum += red[w * kOut + o];
+  auto store = [&](int o, float v) __attribute__((always_inline)) {
     const int ln = o & 63, rr = (o >> 6) & 3, tm = o >> 8;
     const int t = tm / MT, mt = tm % MT;
     const int tile = t * nblocks + (int)blockIdx.x;
     const int m = 16 * mt + 4 * (ln >> 4) + rr;
     const int n = min(16 * tile, N - 16) + (ln & 15);
-    if (tile < NT && m < M && n >= 16 * tile && n < N) Y[(int64_t)m * N + n] = sum;
+    if (tile < NT && m < M && n >= 16 * tile && n < N) Y[(int64_t)m * N + n] = v;
+  };
+  float *const mine = S > 1 ? part + ((int64_t)blockIdx.x * S + split) * kOut : nullptr;
+  for (int o = tid; o < kOut; o += kThreads) {
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) sum += red[w * kOut + o];
+    if (S == 1)
+      store(o, sum);
+    else  // agent-coherent store: straight to the point all XCDs see
+      __hip_atomic_store(mine + o, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (S == 1) return;
+  // K-splits: the last split of this workgroup's tiles to finish adds the S
+  // partials in split order and re-arms the counter (the ordering argument of
+  // the pair-step kernel's splits: agent-scope atomic stores and loads at the
+  // coherence point, vmcnt(0) and the barrier before the increment, loads only
+  // after it returned the final count)
+  __shared__ int last;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's partial stores are done
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev =
+        __hip_atomic_fetch_add(cnt + blockIdx.x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = prev == (uint32_t)(S - 1);
+    if (last) __hip_atomic_store(cnt + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!last) return;
+  const float *const all = part + (int64_t)blockIdx.x * S * kOut;
+  for (int o = tid; o < kOut; o += kThreads) {
+    float sum = __hip_atomic_load(all + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int q = 1; q < S; ++q)
+      sum += __hip_atomic_load(all + (int64_t)q * kOut + o, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    store(o, sum);
   }
 }
 
@@ -950,25 +989,31 @@ hipError_t go_quad_plan(const uint8_t *codes, const uint16_t *scales, int N, int
   }
 }
 
+struct StreamPlan {
+  int ns, it, nb, S;  // steps per wave, tiles per workgroup, workgroups per split, K-splits
+};
+
 template <int MR, int NS, int IT>
 hipError_t go_stream(const uint8_t *codes, const uint16_t *scales, int N, int K, const uint16_t *X,
-                     int M, float *Y, int nblocks, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_mfma_stream_kernel<MR, NS, IT>), dim3(nblocks), dim3(kThreads), 0,
-                     stream, codes, scales, X, Y, N, K, M, nblocks);
+                     int M, float *Y, const StreamPlan &p, uint32_t *cnt, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_mfma_stream_kernel<MR, NS, IT>), dim3(p.nb, p.S), dim3(kThreads), 0,
+                     stream, codes, scales, X, Y, N, K, M, p.nb, p.S, cnt);
   return hipGetLastError();
 }
 
 template <int MR, int NS>
-hipError_t go_stream_it(int it, const uint8_t *codes, const uint16_t *scales, int N, int K,
-                        const uint16_t *X, int M, float *Y, int nb, hipStream_t s) {
-  switch (it) {
-    case 2: return go_stream<MR, NS, 2>(codes, scales, N, K, X, M, Y, nb, s);
-    case 3: return go_stream<MR, NS, 3>(codes, scales, N, K, X, M, Y, nb, s);
-    case 4: return go_stream<MR, NS, 4>(codes, scales, N, K, X, M, Y, nb, s);
-    case 5: return go_stream<MR, NS, 5>(codes, scales, N, K, X, M, Y, nb, s);
-    case 6: return go_stream<MR, NS, 6>(codes, scales, N, K, X, M, Y, nb, s);
-    case 7: return go_stream<MR, NS, 7>(codes, scales, N, K, X, M, Y, nb, s);
-    default: return go_stream<MR, NS, 8>(codes, scales, N, K, X, M, Y, nb, s);
+hipError_t go_stream_it(const uint8_t *codes, const uint16_t *scales, int N, int K,
+                        const uint16_t *X, int M, float *Y, const StreamPlan &p, uint32_t *cnt,
+                        hipStream_t s) {
+  switch (p.it) {
+    case 1: return go_stream<MR, NS, 1>(codes, scales, N, K, X, M, Y, p, cnt, s);
+    case 2: return go_stream<MR, NS, 2>(codes, scales, N, K, X, M, Y, p, cnt, s);
+    case 3: return go_stream<MR, NS, 3>(codes, scales, N, K, X, M, Y, p, cnt, s);
+    case 4: return go_stream<MR, NS, 4>(codes, scales, N, K, X, M, Y, p, cnt, s);
+    case 5: return go_stream<MR, NS, 5>(codes, scales, N, K, X, M, Y, p, cnt, s);
+    case 6: return go_stream<MR, NS, 6>(codes, scales, N, K, X, M, Y, p, cnt, s);
+    case 7: return go_stream<MR, NS, 7>(codes, scales, N, K, X, M, Y, p, cnt, s);
+    default: return go_stream<MR, NS, 8>(codes, scales, N, K, X, M, Y, p, cnt, s);
   }
 }
 
@@ -981,33 +1026,57 @@ hipError_t go_stream_it(int it, const uint8_t *codes, const uint16_t *scales, in
 // Against the pair step (M = 9..32): gate|up 28672 x 4096 at M = 12, 16, 32
 // 29.6, 30.3, 35.6 -> 19.5, 20.0, 26.0 us; at two tiles per CU (q|k|v, 6144
 // rows) even or behind (M = 32: 14.8 vs 14.5), so from three.
-bool stream_plan(int N, int K, int M, int &ns, int &it, int &nb) {
+//
+// With a workspace, M <= 8 and 257 to 512 tiles (which leave half the CUs with
+// two tiles and half with one), K is split in two over workgroups of 3 or 4
+// tiles instead, so that every CU streams the same share (q|k|v 6144 x 4096 at
+// M = 8: 9.3 -> 8.8 us).  Where the tiles already spread evenly the split's
+// exchange of partial tiles, three more memory round trips in a row, costs more
+// than it saves: one tile per CU in two or four splits, o 4096 x 4096 and down
+// 4096 x 14336 at M = 8, 6.1 -> 7.4 and 13.3 -> 15.8 us.
+bool stream_plan(int N, int K, int M, bool split, StreamPlan &p) {
   const int NQ = (K >> 6) >> 2;
   const int tiles = (N + 15) / 16;
-  ns = (NQ + kWaves - 1) / kWaves;
-  nb = std::min(tiles, kCUs);
-  it = (tiles + nb - 1) / nb;
-  return M >= 1 && M <= 32 && (K >> 6) % 4 == 0 && tiles > kCUs && ns >= 1 &&
-         ns <= (M <= 8 ? 4 : 2) && it >= (M <= 8 ? 2 : 3) && it <= 8;
+  if (M < 1 || M > 32 || (K >> 6) % 4 != 0 || N < 16) return false;
+  const int nsmax = M <= 8 ? 4 : 2;
+  if (split && M <= 8 && tiles > kCUs && tiles <= 2 * kCUs && NQ >= 16) {
+    p.S = 2;
+    p.it = (tiles * p.S + kCUs - 1) / kCUs;
+    p.nb = (tiles + p.it - 1) / p.it;
+    p.ns = ((NQ + p.S - 1) / p.S + kWaves - 1) / kWaves;
+    if (p.ns <= nsmax && p.it <= 8 && p.nb <= kSplitCounters) return true;
+  }
+  p.S = 1;
+  p.ns = (NQ + kWaves - 1) / kWaves;
+  p.nb = std::min(tiles, kCUs);
+  p.it = (tiles + p.nb - 1) / p.nb;
+  return tiles > kCUs && p.ns >= 1 && p.ns <= nsmax && p.it >= (M <= 8 ? 2 : 3) && p.it <= 8;
+}
+
+int64_t stream_workspace_bytes(int M, const StreamPlan &p) {
+  if (p.S == 1) return 0;
+  const int MT = M <= 16 ? 1 : 2;
+  return kSplitCounterBytes + (int64_t)p.nb * p.S * p.it * MT * 256 * 4;
 }
 
 template <int MR>
-hipError_t go_stream_ns(int ns, int it, const uint8_t *codes, const uint16_t *scales, int N,
-                        int K, const uint16_t *X, int M, float *Y, int nb, hipStream_t s) {
-  switch (ns) {
-    case 1: return go_stream_it<MR, 1>(it, codes, scales, N, K, X, M, Y, nb, s);
-    case 2: return go_stream_it<MR, 2>(it, codes, scales, N, K, X, M, Y, nb, s);
-    case 3: return go_stream_it<MR, MR == 8 ? 3 : 2>(it, codes, scales, N, K, X, M, Y, nb, s);
-    default: return go_stream_it<MR, MR == 8 ? 4 : 2>(it, codes, scales, N, K, X, M, Y, nb, s);
+hipError_t go_stream_ns(const uint8_t *codes, const uint16_t *scales, int N, int K,
+                        const uint16_t *X, int M, float *Y, const StreamPlan &p, uint32_t *cnt,
+                        hipStream_t s) {
+  switch (p.ns) {
+    case 1: return go_stream_it<MR, 1>(codes, scales, N, K, X, M, Y, p, cnt, s);
+    case 2: return go_stream_it<MR, 2>(codes, scales, N, K, X, M, Y, p, cnt, s);
+    case 3: return go_stream_it<MR, MR == 8 ? 3 : 2>(codes, scales, N, K, X, M, Y, p, cnt, s);
+    default: return go_stream_it<MR, MR == 8 ? 4 : 2>(codes, scales, N, K, X, M, Y, p, cnt, s);
   }
 }
 
 hipError_t go_stream_plan(const uint8_t *codes, const uint16_t *scales, int N, int K,
-                          const uint16_t *X, int M, float *Y, int ns, int it, int nb,
+                          const uint16_t *X, int M, float *Y, const StreamPlan &p, uint32_t *cnt,
                           hipStream_t s) {
-  if (M <= 8) return go_stream_ns<8>(ns, it, codes, scales, N, K, X, M, Y, nb, s);
-  if (M <= 16) return go_stream_ns<16>(ns, it, codes, scales, N, K, X, M, Y, nb, s);
-  return go_stream_ns<32>(ns, it, codes, scales, N, K, X, M, Y, nb, s);
+  if (M <= 8) return go_stream_ns<8>(codes, scales, N, K, X, M, Y, p, cnt, s);
+  if (M <= 16) return go_stream_ns<16>(codes, scales, N, K, X, M, Y, p, cnt, s);
+  return go_stream_ns<32>(codes, scales, N, K, X, M, Y, p, cnt, s);
 }
 
 // Pair-step plan: TB column tiles per workgroup and S K-splits.  Without a
@@ -1069,13 +1138,18 @@ bool quad_shape(int K, int M) { return M <= 8 && (K >> 6) % 4 == 0; }
 }  // namespace
 
 bool gemm_mfma_streams(int64_t N, int64_t K, int M) {
-  int ns, it, nb;
-  return stream_plan((int)N, (int)K, M, ns, it, nb);
+  StreamPlan p;
+  return stream_plan((int)N, (int)K, M, false, p);
 }
 
 int64_t gemm_mfma_workspace_bytes(int64_t N, int64_t K, int M) {
-  if (M < 1 || M > 32 || (K >> 6) % 2 != 0 || quad_shape((int)K, M)) return 0;
-  return pair_workspace_bytes((int)N, M, plan_pair((int)N, (int)K, M, true));
+  if (M < 1 || M > 32 || (K >> 6) % 2 != 0) return 0;
+  StreamPlan sp;
+  const int64_t stream_need =
+      stream_plan((int)N, (int)K, M, true, sp) ? stream_workspace_bytes(M, sp) : 0;
+  if (quad_shape((int)K, M)) return stream_need;
+  return std::max(stream_need,
+                  pair_workspace_bytes((int)N, M, plan_pair((int)N, (int)K, M, true)));
 }
 
 hipError_t launch_gemm_mfma(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
@@ -1086,9 +1160,12 @@ hipError_t launch_gemm_mfma(const uint8_t *codes, const uint16_t *scales, int64_
   // pair steps need an even group count and 4-byte aligned scales (every model
   // shape); otherwise one group per step
   const bool aligned8 = (reinterpret_cast<uintptr_t>(scales) & 7) == 0;
-  int ns, it, nb;
-  if (aligned8 && stream_plan(n, k, M, ns, it, nb))
-    return go_stream_plan(codes, scales, n, k, X, M, Y, ns, it, nb, stream);
+  StreamPlan sp;
+  if (aligned8 && stream_plan(n, k, M, workspace != nullptr, sp)) {
+    if (sp.S > 1 && workspace_bytes < stream_workspace_bytes(M, sp)) return hipErrorInvalidValue;
+    return go_stream_plan(codes, scales, n, k, X, M, Y, sp, static_cast<uint32_t *>(workspace),
+                          stream);
+  }
   if (quad_shape(k, M) && aligned8) return go_quad_plan(codes, scales, n, k, X, M, Y, stream);
   const bool pair = ((k >> 6) % 2 == 0) && ((reinterpret_cast<uintptr_t>(scales) & 3) == 0);
   if (pair) {

@@ -124,14 +124,18 @@ def test_prefill_null_and_alignment(lib):
 def test_smallm_workspace_sizes(lib):
     wb = lib.nf4_gemm_smallm_workspace_bytes
     assert wb(0, 64, 8) == -1 and wb(4, 100, 8) == -1 and wb(4, 64, 0) == -1 and wb(4, 64, 33) == -1
-    assert wb(4096, 4096, 4) == 0          # vector-ALU path: never splits
+    assert wb(6144, 4096, 2) == 0          # vector-ALU path: never splits
     assert wb(28672, 4096, 32) == 0        # enough column tiles for every CU
     assert wb(4096, 4096, 16) == 0         # K = 4096 at M <= 16: splitting does not pay
-    assert wb(4096, 14336, 4) == 0         # M = 4 on the matrix cores: neither
+    assert wb(4096, 4096, 4) == 0          # M <= 8, one tile per CU: no split
+    assert wb(4096, 14336, 4) == 0
+    assert wb(6144, 4096, 5) > 0           # 257 to 512 tiles: streaming form, 2 splits
+    assert wb(28672, 4096, 8) == 0         # ... but not over 512 tiles
+    assert wb(6144, 2048, 8) == 0          # ... nor below 4096 of K
     assert wb(4096, 4096, 32) > 0          # one tile per CU at M > 16: two splits
     assert wb(6144, 4096, 32) > 0          # fewer workgroups than CUs: three tiles, two splits
     assert wb(4096, 14336, 16) > 0         # long K at M 5..16: two tiles, two splits
-    assert wb(4096, 14336, 8) == 0         # ...except M <= 8 with K % 256 == 0 (quad steps)
+    assert wb(4096, 14336, 8) == 0         # M <= 8 with K % 256 == 0, one tile per CU: none
     assert wb(4096, 14464, 8) > 0          # (K = 14464: 226 groups, pair steps, split)
     assert wb(4096, 14336, 32) > 0 and wb(4096, 14336, 32) % 256 == 0
     assert wb(4096, 1024, 32) == 0         # too few pair steps to split

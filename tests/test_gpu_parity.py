@@ -223,9 +223,9 @@ def test_gemm_streaming_form(nf4, M, N, K):
 
 def test_gemm_quad_shape_with_scales_only_4_byte_aligned(nf4):
     """Scales 4 but not 8 bytes aligned: the quad-step shape falls back to the
-    pair-step kernel, without a K-split (no workspace is planned for it)."""
+    pair-step kernel, without a K-split (the workspace planned for the streaming
+    form's split, which needs 8-byte aligned scales, goes unused)."""
     M, N, K = 8, 96, 14336
-    assert nf4.smallm_workspace_bytes(N, K, M) == 0
     W = wl.weights(N, K, 0.02, seed=61, device=DEV)
     codes, scales = _pack_gpu(nf4, W)[:2]
     buf = torch.zeros(N * (K // 64) + 2, dtype=torch.int16, device=DEV)

@@ -63,7 +63,9 @@ def _rows(N, count, seed):
                                    (32, 1000, 8192), (20, 2000, 16384), (32, 37, 8320),
                                    (8, 4096, 14336), (32, 4096, 4096), (32, 6144, 4096),
                                    (16, 1000, 2048), (16, 4096, 14336), (5, 300, 8192),
-                                   (24, 5000, 2048), (32, 4100, 2048)])
+                                   (24, 5000, 2048), (32, 4100, 2048), (8, 4096, 4096),
+                                   (8, 6144, 4096), (6, 8000, 4096), (7, 4200, 16384),
+                                   (4, 4104, 5120)])
 def test_split_matches_oracle_and_repeats(nf4, M, N, K):
     need = nf4.smallm_workspace_bytes(N, K, M)
     W = wl.weights(N, K, 0.02, seed=N + K + M, device=DEV)
@@ -94,10 +96,16 @@ def test_split_is_used_where_planned(nf4):
     assert nf4.smallm_workspace_bytes(1000, 8192, 32) > 0
     assert nf4.smallm_workspace_bytes(37, 8320, 32) > 0
     assert nf4.smallm_workspace_bytes(4096, 14336, 16) > 0
-    assert nf4.smallm_workspace_bytes(4096, 14336, 8) == 0  # quad steps: no split
+    # M <= 8: the streaming form splits K over 257 to 512 column tiles from 4096
+    # of K; one tile per CU runs the quad steps unsplit
+    assert nf4.smallm_workspace_bytes(4096, 14336, 8) == 0
+    assert nf4.smallm_workspace_bytes(4096, 4096, 8) == 0
+    assert nf4.smallm_workspace_bytes(6144, 4096, 8) > 0
+    assert nf4.smallm_workspace_bytes(4104, 16384, 5) > 0
+    assert nf4.smallm_workspace_bytes(28672, 4096, 8) == 0
+    assert nf4.smallm_workspace_bytes(6144, 2048, 8) == 0
     assert nf4.smallm_workspace_bytes(6144, 4096, 32) > 0
     assert nf4.smallm_workspace_bytes(4096, 4096, 32) > 0
-    assert nf4.smallm_workspace_bytes(4096, 4096, 8) == 0
     assert nf4.smallm_workspace_bytes(28672, 4096, 32) == 0
 
 
