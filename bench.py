@@ -179,19 +179,26 @@ def recorded_traffic(key):
     return None
 
 
-def kernel_label(M, N, K):
+def kernel_label(M, N, K, workspace=True):
     """Name of the kernel a product of this shape runs, by the library's dispatch
     rule (a label for the bench line only): the vector-ALU GEMV for M <= 2 and for
     M = 3, 4 above 5120 rows (but M = 4 above 16384 rows where the streaming form
     takes it); with K a multiple of 256, the streaming MFMA form when there are
     more 16-column tiles than CUs (2 to 8 per CU at M <= 8 with at most 4 steps of
-    256 per wave, 3 to 8 per CU above with at most 2); else quad steps for M <= 8,
-    MFMA pair steps up to M = 32; the prefill tiles beyond."""
+    256 per wave, 3 to 8 per CU above with at most 2), or, given a workspace, with
+    K split over up to 512 tiles (from 4096 of K; at M <= 8 only above 256 tiles);
+    else quad steps for M <= 8, MFMA pair steps up to M = 32; the prefill tiles
+    beyond."""
     tiles, steps = (N + 15) // 16, K // 256
     per_cu = -(-tiles // 256)
-    streams = (M <= 32 and K % 256 == 0 and tiles > 256
-               and -(-steps // 8) <= (4 if M <= 8 else 2)
+    nsmax = 4 if M <= 8 else 2
+    streams = (M <= 32 and K % 256 == 0 and tiles > 256 and -(-steps // 8) <= nsmax
                and (2 if M <= 8 else 3) <= per_cu <= 8)
+    if (workspace and M <= 32 and K % 256 == 0 and N >= 16 and tiles <= 512 and steps >= 16
+            and (M > 8 or tiles > 256)):
+        S = 2 if M <= 8 or steps <= 16 else 4
+        it = S if tiles <= 256 else -(-(tiles * S) // 256)
+        streams = streams or (-(-(-(-steps // S)) // 8) <= nsmax and it <= 8)
     if (M <= 2 or (M <= 4 and N > 5120)) and not (M == 4 and N > 16384 and streams):
         return "gemv_valu_kernel"
     if streams:

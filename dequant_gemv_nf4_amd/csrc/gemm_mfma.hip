@@ -680,7 +680,7 @@ __global__ void __launch_bounds__(kThreads)
 // the same moment (q|k|v 6144 x 4096 at M = 8: 10.2 -> 9.4 us).  Llama-3.1-8B
 // gate|up (28672 x 4096) at M = 8: 26.0 -> 19 us against the quad step.
 // ---------------------------------------------------------------------------
-template <int MR, int NS, int IT>
+template <int MR, int NS, int IT, bool SW>
 __global__ void __launch_bounds__(kThreads)
     gemm_mfma_stream_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
                             const uint16_t *__restrict__ X, float *__restrict__ Y, int N, int K,
@@ -760,7 +760,13 @@ __global__ void __launch_bounds__(kThreads)
 
   constexpr int kRing = IT < 2 ? IT : 2;  // tiles in flight
   u32x4_t rc[kRing][NS][2];
+  // scales: one 8-byte load per step, or (SW: every wave of the launch owns
+  // exactly NS steps, NS even) one 16-byte load per two steps.  A load touches
+  // the 16 rows' lines either way, and the memory pipeline's cost follows the
+  // lines an instruction touches, so SW halves the cost of the scales.
+  constexpr int kScaleLoads = SW ? NS / 2 : NS;
   u32x2_t rs[kRing][NS];
+  u32x4_t rsw[kRing][SW ? NS / 2 : 1];
   auto load_tile = [&](auto slot, int t) __attribute__((always_inline)) {
     constexpr int d = decltype(slot)::value;
     const int tb = tile_row(t);
@@ -770,7 +776,12 @@ __global__ void __launch_bounds__(kThreads)
       const int coff = tb * (K >> 1) + 128 * q;
       rc[d][s][0] = __builtin_amdgcn_raw_buffer_load_b128(crs, cv0, coff, kLoadStream);
       rc[d][s][1] = __builtin_amdgcn_raw_buffer_load_b128(crs, cv1, coff, kLoadStream);
-      rs[d][s] = __builtin_amdgcn_raw_buffer_load_b64(srs, svo, tb * NG * 2 + 8 * q, 0);
+      if constexpr (!SW) rs[d][s] = __builtin_amdgcn_raw_buffer_load_b64(srs, svo, tb * NG * 2 + 8 * q, 0);
+    }
+    if constexpr (SW) {
+#pragma unroll
+      for (int j = 0; j < kScaleLoads; ++j)
+        rsw[d][j] = __builtin_amdgcn_raw_buffer_load_b128(srs, svo, tb * NG * 2 + 8 * (q0 + 2 * j), 0);
     }
   };
 
@@ -805,7 +816,13 @@ __global__ void __launch_bounds__(kThreads)
         r[4 + e] = hi[0];
         r[6 + e] = hi[1];
       }
-      const u32x2_t sw = rs[d][s];
+      u32x2_t sw;
+      if constexpr (SW) {
+        sw[0] = rsw[d][s >> 1][2 * (s & 1)];
+        sw[1] = rsw[d][s >> 1][2 * (s & 1) + 1];
+      } else {
+        sw = rs[d][s];
+      }
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         f32x4_t g[MT];
@@ -996,8 +1013,15 @@ struct StreamPlan {
 template <int MR, int NS, int IT>
 hipError_t go_stream(const uint8_t *codes, const uint16_t *scales, int N, int K, const uint16_t *X,
                      int M, float *Y, const StreamPlan &p, uint32_t *cnt, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_mfma_stream_kernel<MR, NS, IT>), dim3(p.nb, p.S), dim3(kThreads), 0,
-                     stream, codes, scales, X, Y, N, K, M, p.nb, p.S, cnt);
+  // wide scale loads when every wave's slice is exactly NS steps, NS even
+  const int NQ = (K >> 6) >> 2;
+  const bool wide = NS % 2 == 0 && NQ % (p.S * kWaves) == 0 && NQ / (p.S * kWaves) == NS;
+  if (wide)
+    hipLaunchKernelGGL((gemm_mfma_stream_kernel<MR, NS, IT, NS % 2 == 0>), dim3(p.nb, p.S),
+                       dim3(kThreads), 0, stream, codes, scales, X, Y, N, K, M, p.nb, p.S, cnt);
+  else
+    hipLaunchKernelGGL((gemm_mfma_stream_kernel<MR, NS, IT, false>), dim3(p.nb, p.S),
+                       dim3(kThreads), 0, stream, codes, scales, X, Y, N, K, M, p.nb, p.S, cnt);
   return hipGetLastError();
 }
 
@@ -1027,21 +1051,28 @@ hipError_t go_stream_it(const uint8_t *codes, const uint16_t *scales, int N, int
 // 29.6, 30.3, 35.6 -> 19.5, 20.0, 26.0 us; at two tiles per CU (q|k|v, 6144
 // rows) even or behind (M = 32: 14.8 vs 14.5), so from three.
 //
-// With a workspace, M <= 8 and 257 to 512 tiles (which leave half the CUs with
-// two tiles and half with one), K is split in two over workgroups of 3 or 4
-// tiles instead, so that every CU streams the same share (q|k|v 6144 x 4096 at
-// M = 8: 9.3 -> 8.8 us).  Where the tiles already spread evenly the split's
-// exchange of partial tiles, three more memory round trips in a row, costs more
-// than it saves: one tile per CU in two or four splits, o 4096 x 4096 and down
-// 4096 x 14336 at M = 8, 6.1 -> 7.4 and 13.3 -> 15.8 us.
+// With a workspace, up to 512 tiles and at least 4096 of K, K is split over
+// workgroups of several tiles instead, so that a CU reads only its share of
+// the activations and every CU streams the same share of the codes:
+//  - M <= 8, 257 to 512 tiles (which leave half the CUs with two tiles and half
+//    with one): two splits (q|k|v 6144 x 4096 at M = 8: 9.3 -> 8.8 us).  At one
+//    tile per CU the split's exchange of partial tiles, three more memory round
+//    trips in a row, costs more than it saves (o 4096 x 4096 and down 4096 x
+//    14336 at M = 8 in two and four splits: 6.1 -> 7.4 and 13.3 -> 15.8 us);
+//  - M = 9..32, where the activations a one-tile CU reads are 2 to 8 times its
+//    codes: two splits up to 4096 of K, four above, each workgroup taking as
+//    many tiles as splits (against the pair step's own splits at M = 32: q|k|v
+//    15.7 -> 12.2 us, o 11.0 -> 10.5, down 4096 x 14336 26.7 -> 23.5; at M = 16
+//    10.5 -> 9.3, 8.2 -> 7.9, 17.8 -> 16.9; twice as many splits ran 30-60 %
+//    slower).
 bool stream_plan(int N, int K, int M, bool split, StreamPlan &p) {
   const int NQ = (K >> 6) >> 2;
   const int tiles = (N + 15) / 16;
   if (M < 1 || M > 32 || (K >> 6) % 4 != 0 || N < 16) return false;
   const int nsmax = M <= 8 ? 4 : 2;
-  if (split && M <= 8 && tiles > kCUs && tiles <= 2 * kCUs && NQ >= 16) {
-    p.S = 2;
-    p.it = (tiles * p.S + kCUs - 1) / kCUs;
+  if (split && tiles <= 2 * kCUs && NQ >= 16 && (M > 8 || tiles > kCUs)) {
+    p.S = M <= 8 || NQ <= 16 ? 2 : 4;
+    p.it = tiles <= kCUs ? p.S : (tiles * p.S + kCUs - 1) / kCUs;
     p.nb = (tiles + p.it - 1) / p.it;
     p.ns = ((NQ + p.S - 1) / p.S + kWaves - 1) / kWaves;
     if (p.ns <= nsmax && p.it <= 8 && p.nb <= kSplitCounters) return true;

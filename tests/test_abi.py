@@ -126,7 +126,7 @@ def test_smallm_workspace_sizes(lib):
     assert wb(0, 64, 8) == -1 and wb(4, 100, 8) == -1 and wb(4, 64, 0) == -1 and wb(4, 64, 33) == -1
     assert wb(6144, 4096, 2) == 0          # vector-ALU path: never splits
     assert wb(28672, 4096, 32) == 0        # enough column tiles for every CU
-    assert wb(4096, 4096, 16) == 0         # K = 4096 at M <= 16: splitting does not pay
+    assert wb(4096, 4096, 16) > 0          # M = 9..32: the streaming form splits K in two
     assert wb(4096, 4096, 4) == 0          # M <= 8, one tile per CU: no split
     assert wb(4096, 14336, 4) == 0
     assert wb(6144, 4096, 5) > 0           # 257 to 512 tiles: streaming form, 2 splits

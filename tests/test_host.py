@@ -123,8 +123,9 @@ def test_build_record_matches_the_sources():
     (4, 57344, 8192, "gemv_valu_kernel"), (8, 6144, 4096, "gemm_mfma_stream_kernel"),
     (3, 4096, 14336, "gemm_mfma_quad_kernel"), (8, 28672, 4096, "gemm_mfma_stream_kernel"),
     (8, 8192, 28672, "gemm_mfma_quad_kernel"),
-    (8, 4096, 14464, "gemm_mfma_pair_kernel"), (16, 4096, 4096, "gemm_mfma_pair_kernel"),
-    (16, 6144, 4096, "gemm_mfma_pair_kernel"), (16, 28672, 4096, "gemm_mfma_stream_kernel"),
+    (8, 4096, 14464, "gemm_mfma_pair_kernel"), (16, 4096, 4096, "gemm_mfma_stream_kernel"),
+    (16, 6144, 4096, "gemm_mfma_stream_kernel"), (16, 28672, 4096, "gemm_mfma_stream_kernel"),
+    (32, 4096, 14336, "gemm_mfma_stream_kernel"), (8, 4096, 14336, "gemm_mfma_quad_kernel"),
     (32, 28672, 4096, "gemm_mfma_stream_kernel"), (32, 28672, 5120, "gemm_mfma_pair_kernel"),
     (32, 100, 320, "gemm_mfma_kernel"), (64, 4096, 4096, "gemm_prefill_kernel")])
 def test_bench_kernel_label(M, N, K, name):
