@@ -192,13 +192,15 @@ def kernel_label(M, N, K, workspace=True):
     tiles, steps = (N + 15) // 16, K // 256
     per_cu = -(-tiles // 256)
     nsmax = 4 if M <= 8 else 2
-    streams = (M <= 32 and K % 256 == 0 and tiles > 256 and -(-steps // 8) <= nsmax
-               and (2 if M <= 8 else 3) <= per_cu <= 8)
+    ns = -(-steps // 8)
+    streams = (M <= 32 and K % 256 == 0 and tiles > 256 and ns <= nsmax
+               and (2 if M <= 8 else 3) <= per_cu <= (5 if ns == 4 else 8))
     if (workspace and M <= 32 and K % 256 == 0 and N >= 16 and tiles <= 512 and steps >= 16
             and (M > 8 or tiles > 256)):
         S = 2 if M <= 8 or steps <= 16 else 4
         it = S if tiles <= 256 else -(-(tiles * S) // 256)
-        streams = streams or (-(-(-(-steps // S)) // 8) <= nsmax and it <= 8)
+        nss = -(-(-(-steps // S)) // 8)
+        streams = streams or (nss <= nsmax and it <= (5 if nss == 4 else 8))
     if (M <= 2 or (M <= 4 and N > 5120)) and not (M == 4 and N > 16384 and streams):
         return "gemv_valu_kernel"
     if streams:

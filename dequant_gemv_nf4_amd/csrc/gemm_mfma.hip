@@ -51,6 +51,8 @@
 namespace nf4 {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -105,6 +107,28 @@ __device__ __forceinline__ u32x2_t lds_load_u64(const uint32_t *base, uint32_t b
 __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t mfma_f16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// the wave's largest (Max) or smallest of a 32-bit value, as a scalar
+template <bool Max>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
+  auto f = [](uint32_t a, uint32_t b) { return Max ? max(a, b) : min(a, b); };
+  // (the DPP source of a lane outside the row pattern is never read: every
+  // control below pairs lanes within a row of 16)
+  v = f(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xf, 0xf, false));
+  v = f(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xf, 0xf, false));
+  v = f(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xf, 0xf, false));
+  v = f(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xf, 0xf, false));
+  const uint32_t a = f((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+                       (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const uint32_t b = f((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
+                       (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return f(a, b);
 }
 
 template <int d>
@@ -680,7 +704,7 @@ __global__ void __launch_bounds__(kThreads)
 // the same moment (q|k|v 6144 x 4096 at M = 8: 10.2 -> 9.4 us).  Llama-3.1-8B
 // gate|up (28672 x 4096) at M = 8: 26.0 -> 19 us against the quad step.
 // ---------------------------------------------------------------------------
-template <int MR, int NS, int IT, bool SW>
+template <int MR, int NS, int IT, bool SW, bool F16>
 __global__ void __launch_bounds__(kThreads)
     gemm_mfma_stream_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
                             const uint16_t *__restrict__ X, float *__restrict__ Y, int N, int K,
@@ -758,6 +782,9 @@ __global__ void __launch_bounds__(kThreads)
               __builtin_amdgcn_raw_buffer_load_b128(xrs, xvo[mt] + 128 * gq + 16 * h, 512 * q, 0);
   }
 
+  uint32_t wide = 0;  // bit 4 s + gq: group gq of slot s is added exactly (below)
+  float gfac[NS][4];  // 2^(Emax - 141): undoes the group's f16 shift
+
   constexpr int kRing = IT < 2 ? IT : 2;  // tiles in flight
   u32x4_t rc[kRing][NS][2];
   // scales: one 8-byte load per step, or (SW: every wave of the launch owns
@@ -791,7 +818,9 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const uint32_t laneoff = 8u * (lane & 31);
+  // table lane offsets: copy lane % 32 of 4-byte f16-pair entries (F16) or of
+  // 8-byte (hi pair, lo pair) entries
+  const uint32_t laneoff = F16 ? lut_lane_offset(lane) : 8u * (lane & 31);
   auto compute = [&](auto slot, f32x4_t (&ac)[MT]) __attribute__((always_inline)) {
     constexpr int d = decltype(slot)::value;
 #pragma unroll
@@ -829,20 +858,31 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const uint32_t w = r[2 * gq + h];
-          u32x4_t bh, bl;
-          u32x2_t e;
-          e = lds_load_u64(lds, split_addr<0>(w, laneoff)); bh[0] = e[0]; bl[0] = e[1];
-          e = lds_load_u64(lds, split_addr<1>(w, laneoff)); bh[1] = e[0]; bl[1] = e[1];
-          e = lds_load_u64(lds, split_addr<2>(w, laneoff)); bh[2] = e[0]; bl[2] = e[1];
-          e = lds_load_u64(lds, split_addr<3>(w, laneoff)); bh[3] = e[0]; bl[3] = e[1];
+          if constexpr (F16) {
+            const u32x4_t b = {lds_load_u32(lds, lut_addr<0>(w, laneoff)),
+                               lds_load_u32(lds, lut_addr<1>(w, laneoff)),
+                               lds_load_u32(lds, lut_addr<2>(w, laneoff)),
+                               lds_load_u32(lds, lut_addr<3>(w, laneoff))};
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            g[mt] = mfma_bf16(A[s][mt][gq][h], bh, h == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : g[mt]);
-            g[mt] = mfma_bf16(A[s][mt][gq][h], bl, g[mt]);
+            for (int mt = 0; mt < MT; ++mt)
+              g[mt] = mfma_f16(A[s][mt][gq][h], b, h == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : g[mt]);
+          } else {
+            u32x4_t bh, bl;
+            u32x2_t e;
+            e = lds_load_u64(lds, split_addr<0>(w, laneoff)); bh[0] = e[0]; bl[0] = e[1];
+            e = lds_load_u64(lds, split_addr<1>(w, laneoff)); bh[1] = e[0]; bl[1] = e[1];
+            e = lds_load_u64(lds, split_addr<2>(w, laneoff)); bh[2] = e[0]; bl[2] = e[1];
+            e = lds_load_u64(lds, split_addr<3>(w, laneoff)); bh[3] = e[0]; bl[3] = e[1];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              g[mt] = mfma_bf16(A[s][mt][gq][h], bh, h == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : g[mt]);
+              g[mt] = mfma_bf16(A[s][mt][gq][h], bl, g[mt]);
+            }
           }
         }
         const uint32_t sword = sw[gq >> 1];
-        const float sc = f16_bits_to_f32((gq & 1) ? (sword >> 16) : (sword & 0xffffu));
+        float sc = f16_bits_to_f32((gq & 1) ? (sword >> 16) : (sword & 0xffffu));
+        if constexpr (F16) sc *= gfac[s][gq];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -854,7 +894,63 @@ __global__ void __launch_bounds__(kThreads)
   load_tile(Slot<0>{}, 0);
   if constexpr (IT > 1) load_tile(Slot<1>{}, 1);
   __builtin_amdgcn_sched_barrier(0);
-  build_split_lut(lds, lane, wave);
+  if constexpr (F16)
+    build_byte_lut(lds, tid, kThreads);
+  else
+    build_split_lut(lds, lane, wave);
+  // F16: activations to f16, one power-of-two shift per group of 64 k shared by all
+  // rows: the group's largest |x| (a max over the whole wave, which holds every
+  // row of the group) goes to [2^14, 2^15), on the bit patterns (subtract
+  // (Emax - 29) << 7 from each bf16 magnitude, saturating, and shift left by 3
+  // into the f16 fields).  Exact unless a non-zero value lands below the f16
+  // normals (more than 2^28 under the largest) or the largest is under 2^-98:
+  // such a group is flagged, its tiles are multiplied by 0 instead of undoing
+  // the shift (the staged values are finite: the largest f16 exponent field is
+  // 29), and its terms are added exactly after the tiles.  Otherwise the shift
+  // is undone, with the column's scale, on the group's fp32 tile.
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      if constexpr (!F16) continue;
+      // the group's largest magnitude and its smallest non-zero one, less 1
+      // (zero wraps to 0xffff), as bf16 bit patterns
+      u16x2 pm = {0, 0}, pn = {0xffff, 0xffff};
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int h = 0; h < (MR == 8 ? 1 : 2); ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const u16x2 mag = __builtin_bit_cast(u16x2, A[s][mt][gq][h][e] & 0x7fff7fffu);
+            pm = __builtin_elementwise_max(pm, mag);
+            pn = __builtin_elementwise_min(pn, mag - (u16x2){1, 1});
+          }
+      const uint32_t mx = wave_reduce_u32<true>(max((uint32_t)pm[0], (uint32_t)pm[1]));
+      const uint32_t mnm1 = wave_reduce_u32<false>(min((uint32_t)pn[0], (uint32_t)pn[1]));
+      const uint32_t emax = mx >> 7;
+      const uint32_t bias = ((emax - 29u) << 7) & 0xffffu;
+      const u16x2 bias2 = __builtin_bit_cast(u16x2, bias * 0x10001u);
+      // lost: a non-zero magnitude at or below bias + 0x7f (an exponent field of
+      // 0 or less after the subtraction)
+      const bool gw = mx != 0 && (emax < 29u || mnm1 < bias + 0x7fu);
+      wide |= gw ? 1u << (4 * s + gq) : 0u;
+      gfac[s][gq] = gw || mx == 0 ? 0.0f : __uint_as_float((emax - 14u) << 23);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int h = 0; h < (MR == 8 ? 1 : 2); ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t w = A[s][mt][gq][h][e];
+            const u16x2 mag = __builtin_bit_cast(u16x2, w & 0x7fff7fffu);
+            const uint32_t f = __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(mag, bias2)
+                                                                << (u16x2){3, 3}) |
+                               (w & 0x80008000u);
+            A[s][mt][gq][h][e] = f;
+          }
+      __builtin_amdgcn_sched_barrier(0);  // one group at a time (registers)
+    }
   // MR = 8: the second half of each activation fragment comes from lane n +- 8
   // of the row, which loaded it (a DPP row rotation by 8)
   if constexpr (MR == 8) {
@@ -889,6 +985,41 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
         red[(((slice * IT + t) * MT + mt) * 4 + rr) * 64 + lane] = acc[t][mt][rr];
+  // ---- exact pass for the groups f16 could not hold (only in waves that have
+  // one; about 1e-8 of the groups of N(0, 1) data).  The row loop added nothing
+  // for such a group.  Lane (n, g) adds to its own partials in LDS, for column n
+  // of each tile and its rows 4 g + rr of each row tile, every term of the group
+  // as (fp32 level x fp32 scale) x bf16 activation with one fp32 fma: each term
+  // rounded once, no partial sum formed before the scale is applied.
+  if (F16 && wide != 0) {
+#pragma unroll 1
+    for (int sg = 0; sg < 4 * NS; ++sg) {
+      if ((wide >> sg & 1u) == 0 || (sg >> 2) >= ns) continue;
+      const int G = 4 * step_of(sg >> 2) + (sg & 3);  // the group's index along K
+#pragma unroll 1
+      for (int t = 0; t < IT; ++t) {
+        const int n = tile_row(t) + col;
+        const uint8_t *cp = codes + (int64_t)n * (K >> 1) + 32 * G;
+        const float sc = f16_bits_to_f32(scales[(int64_t)n * NG + G]);
+#pragma unroll 1
+        for (int mr = 0; mr < 4 * MT; ++mr) {
+          const int m = 16 * (mr >> 2) + 4 * lg + (mr & 3);
+          if (m >= M || (MR == 8 && m >= 8)) continue;
+          const uint16_t *xr = X + (int64_t)m * K + 64 * G;
+          float *slot = red + ((((slice * IT + t) * MT + (mr >> 2)) * 4 + (mr & 3)) * 64 + lane);
+          float v = *slot;
+#pragma unroll 1
+          for (int j = 0; j < 32; ++j) {
+            const uint32_t byte = cp[j];
+            const uint32_t xw = *reinterpret_cast<const uint32_t *>(xr + 2 * j);
+            v = fmaf(level_f32(byte & 15u) * sc, bf16_lo(xw), v);
+            v = fmaf(level_f32(byte >> 4) * sc, bf16_hi(xw), v);
+          }
+          *slot = v;
+        }
+      }
+    }
+  }
   __syncthreads();
   constexpr int kOut = IT * MT * 256;
   auto store = [&](int o, float v) __attribute__((always_inline)) {
@@ -1016,11 +1147,14 @@ hipError_t go_stream(const uint8_t *codes, const uint16_t *scales, int N, int K,
   // wide scale loads when every wave's slice is exactly NS steps, NS even
   const int NQ = (K >> 6) >> 2;
   const bool wide = NS % 2 == 0 && NQ % (p.S * kWaves) == 0 && NQ / (p.S * kWaves) == NS;
+  // f16 products from 5 tiles per workgroup: the per-group shift costs set-up
+  // that shorter walks do not win back
+  constexpr bool F16 = IT >= 5;
   if (wide)
-    hipLaunchKernelGGL((gemm_mfma_stream_kernel<MR, NS, IT, NS % 2 == 0>), dim3(p.nb, p.S),
+    hipLaunchKernelGGL((gemm_mfma_stream_kernel<MR, NS, IT, NS % 2 == 0, F16>), dim3(p.nb, p.S),
                        dim3(kThreads), 0, stream, codes, scales, X, Y, N, K, M, p.nb, p.S, cnt);
   else
-    hipLaunchKernelGGL((gemm_mfma_stream_kernel<MR, NS, IT, false>), dim3(p.nb, p.S),
+    hipLaunchKernelGGL((gemm_mfma_stream_kernel<MR, NS, IT, false, F16>), dim3(p.nb, p.S),
                        dim3(kThreads), 0, stream, codes, scales, X, Y, N, K, M, p.nb, p.S, cnt);
   return hipGetLastError();
 }
@@ -1075,13 +1209,15 @@ bool stream_plan(int N, int K, int M, bool split, StreamPlan &p) {
     p.it = tiles <= kCUs ? p.S : (tiles * p.S + kCUs - 1) / kCUs;
     p.nb = (tiles + p.it - 1) / p.it;
     p.ns = ((NQ + p.S - 1) / p.S + kWaves - 1) / kWaves;
-    if (p.ns <= nsmax && p.it <= 8 && p.nb <= kSplitCounters) return true;
+    if (p.ns <= nsmax && p.it <= 8 && (p.ns < 4 || p.it <= 5) && p.nb <= kSplitCounters)
+      return true;
   }
   p.S = 1;
   p.ns = (NQ + kWaves - 1) / kWaves;
   p.nb = std::min(tiles, kCUs);
   p.it = (tiles + p.nb - 1) / p.nb;
-  return tiles > kCUs && p.ns >= 1 && p.ns <= nsmax && p.it >= (M <= 8 ? 2 : 3) && p.it <= 8;
+  return tiles > kCUs && p.ns >= 1 && p.ns <= nsmax && p.it >= (M <= 8 ? 2 : 3) && p.it <= 8 &&
+         (p.ns < 4 || p.it <= 5);  // (4 steps and 6 tiles spill registers)
 }
 
 int64_t stream_workspace_bytes(int M, const StreamPlan &p) {

@@ -332,6 +332,32 @@ def test_activation_range_planted_on_zero_weights(nf4, M):
     assert np.isfinite(Y.cpu().numpy()).all()
 
 
+@pytest.mark.parametrize("M,N,K", [(8, 16400, 2048), (5, 20480, 1024), (16, 16400, 2048),
+                                   (32, 20480, 1024), (24, 16400, 4096), (8, 8200, 4096)])
+def test_streaming_form_activation_ranges(nf4, M, N, K):
+    """From 5 tiles per workgroup the streaming MFMA form runs f16 products with
+    one power-of-two shift per group of 64 k shared by every row: groups whose
+    entries span more than f16 holds (planted 2^30, 2^40, 2^100 above the rest on
+    zero-level weights, or rows 2^40 apart) go through its exact fp32 pass, the
+    others through f16.  Shapes: the padded 8-row tile (M = 5, 8), one and two
+    16-row tiles (M = 16; 24, 32), slices of one and two steps, some waves with
+    none (K = 1024); and 3 tiles per workgroup, which stays on bf16 hi + lo."""
+    U = K // 32
+    ratios = [2.0 ** 20, 2.0 ** 26, 2.0 ** 30, 2.0 ** 40, 2.0 ** 100]
+    # planted in every 16th unit: most groups exact in f16, the rest wide
+    _planted_range_case(nf4, M, N, K, ratios, units=range(0, U, 16), seed=20 + M)
+    # one row 2^40 below the others: every group is wide through the rows
+    W = wl.weights(N, K, 0.02, seed=31 + M, device=DEV)
+    X = wl.activations(M, K, seed=37 + M).float()
+    X[M // 2] *= 2.0 ** -40
+    Xb = X.to(torch.bfloat16)
+    codes, scales, st = _pack_gpu(nf4, W)
+    ref_p, ref_s, _ = _host_pack(W)
+    Y = _guarded_product(nf4, codes, scales, Xb.to(DEV))
+    Yr, A = oracle.gemm(ref_p, ref_s, wl.bf16_bits(Xb))
+    _check_product(Y, Yr, A, f"rows 2^40 apart M={M} N={N} K={K}")
+
+
 def test_activation_range_in_one_slice_only(nf4):
     """K = 16384 at M = 1 runs four K-slices: only the waves whose slice holds a
     planted unit take the exact fp32 form, the others the f16 form; the slices'
