@@ -43,9 +43,14 @@
  * exact (every non-zero value of the block within 2^28 of its largest in
  * binary exponent, and the largest at least 2^-98); the blocks that are not
  * are computed as f16 level x fp32 scale (exact) times the bf16 activation in
- * fp32 instead.  On the MFMA kernels (every other M, and nf4_gemm_prefill) the
- * levels are split into bf16 hi + lo and the bf16 activations are used as they
- * are.  Per output element
+ * fp32 instead.  The MFMA product that walks 5 or more 16-column tiles per
+ * workgroup (M <= 32 on matrices of 16385 to 32768 rows, K a multiple of 256 and
+ * at most 2048 per wave slice) takes f16 levels and f16 activations
+ * scaled by a power of two per 64-value group shared by all rows, under the
+ * same exactness rule over the group's values of every row; a group that fails
+ * is computed the same exact way.  The other MFMA kernels (every other M, and
+ * nf4_gemm_prefill) split the levels into bf16 hi + lo and use the bf16
+ * activations as they are.  Per output element
  *   |Y - Y_exact| <= 2e-3 * sum_k |w~(n,k) X[m][k]| + 1e-5
  * for finite inputs with every |X[m][k]| <= 2^120 and every
  * sum_k |w~(n,k) X[m][k]| <= 2^120 (w~ = the dequantized weight).  Results are
