@@ -44,8 +44,8 @@
  * binary exponent, and the largest at least 2^-98); the blocks that are not
  * are computed as f16 level x fp32 scale (exact) times the bf16 activation in
  * fp32 instead.  The MFMA product that walks 5 or more 16-column tiles per
- * workgroup (M <= 32 on matrices of 16385 to 32768 rows, K a multiple of 256 and
- * at most 2048 per wave slice) takes f16 levels and f16 activations
+ * workgroup (M <= 32 on matrices of 16385 to 32768 rows, K a multiple of 256 up
+ * to 8192, up to 4096 above M = 8) takes f16 levels and f16 activations
  * scaled by a power of two per 64-value group shared by all rows, under the
  * same exactness rule over the group's values of every row; a group that fails
  * is computed the same exact way.  The other MFMA kernels (every other M, and
