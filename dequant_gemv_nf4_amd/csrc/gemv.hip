@@ -110,12 +110,15 @@ __global__ void __launch_bounds__(kThreads)
 
   int unit[UPL];
   bool valid[UPL];
-  int uload[UPL];  // a lane past its slice loads a real unit of the row; unused
+  // a lane past its slice loads a unit that a lane of the same load instruction
+  // reads anyway (that instruction's first unit, else the slice's first): the
+  // duplicate stays within lines the instruction fetches; its data is unused
+  int uload[UPL];
 #pragma unroll
   for (int i = 0; i < UPL; ++i) {
     unit[i] = ub + lane + 64 * i;
     valid[i] = unit[i] < ue;
-    uload[i] = valid[i] ? unit[i] : 0;
+    uload[i] = valid[i] ? unit[i] : (ub + 64 * i < ue ? ub + 64 * i : ub);
   }
   // scales.  Us is a multiple of 4, so a slice owns whole groups, at most 128 of
   // them, starting at an even group gb.  Unit ub + l + 64 i needs group
@@ -171,25 +174,36 @@ __global__ void __launch_bounds__(kThreads)
   for (int i = 0; i < UPL; ++i) cvo[i] = uload[i] * 16;
 #pragma unroll
   for (int j = 0; j < kScaleLoads; ++j) svo[j] = gload[j] * (WS ? 4 : 2);
-  // Step t of the wave is row r; a step past the wave's last (or a row past N)
-  // loads row `fallback` instead, one the wave has just read, so the spare load
-  // hits in cache.
+  // Step t of the wave is row r.  A step past the wave's last (or a row past N)
+  // still issues its loads, so that the ring's load counts stay the same on every
+  // path, but through descriptors of zero size: a buffer load out of range
+  // returns zeros without a memory access.  (Re-reading a row just read instead
+  // cost HBM traffic under the non-temporal hint, whose lines leave the cache
+  // early: 13B q|k|v read 1.09x its bytes, 1.006x with the empty descriptors.)
+  // The offset then is that of row `fallback`, a real row, so it cannot overflow.
+  const __amdgpu_buffer_rsrc_t crs0 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(codes), 0, 0, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t srs0 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(scales), 0, 0, kBufferWord3);
   auto load_row = [&](int t, int r, int fallback, uint4 *c, ScaleT *s) {
-    const int rr = __builtin_amdgcn_readfirstlane((t < iters && r < N) ? r : fallback);
+    const bool real = t < iters && r < N;  // uniform
+    const int rr = __builtin_amdgcn_readfirstlane(real ? r : fallback);
     const int coff = rr * (int)row_bytes;
     const int soff = rr * (int)row_groups * 2;
+    const __amdgpu_buffer_rsrc_t cr = real ? crs : crs0;
+    const __amdgpu_buffer_rsrc_t sr = real ? srs : srs0;
 #pragma unroll
     for (int i = 0; i < UPL; ++i) {
       const u32x4_nt_t v =
-          __builtin_amdgcn_raw_buffer_load_b128(crs, cvo[i], coff, NT ? kLoadStream : 0);
+          __builtin_amdgcn_raw_buffer_load_b128(cr, cvo[i], coff, NT ? kLoadStream : 0);
       c[i] = make_uint4(v.x, v.y, v.z, v.w);
     }
 #pragma unroll
     for (int j = 0; j < kScaleLoads; ++j) {
       if constexpr (WS)
-        s[j] = __builtin_amdgcn_raw_buffer_load_b32(srs, svo[j], soff, 0);
+        s[j] = __builtin_amdgcn_raw_buffer_load_b32(sr, svo[j], soff, 0);
       else
-        s[j] = __builtin_amdgcn_raw_buffer_load_b16(srs, svo[j], soff, 0);
+        s[j] = __builtin_amdgcn_raw_buffer_load_b16(sr, svo[j], soff, 0);
     }
   };
   uint4 cb[kDepth][UPL];
@@ -374,8 +388,8 @@ __global__ void __launch_bounds__(kThreads)
   };
 
   // Whole rounds of kDepth rows run without branches (rows past N compute on the
-  // wave's first row and are never stored), so the load waits stay exact across
-  // the loop's back edge; the last partial round follows.
+  // zeros their loads returned and are never stored), so the load waits stay
+  // exact across the loop's back edge; the last partial round follows.
   int it = 0;
   for (; it + kDepth <= iters; it += kDepth) {
 #pragma unroll
