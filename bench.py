@@ -179,31 +179,44 @@ def recorded_traffic(key):
     return None
 
 
+def stream_tiles(M, N, K, workspace=True):
+    """Column tiles per workgroup of the streaming MFMA form for this shape, or None
+    where the library does not run it (its plan rule, mirrored for the bench line's
+    labels only): K a multiple of 256 and M <= 32; given a workspace, K split over
+    up to 512 tiles of 16 columns from 4096 of K (two splits at M <= 8 or up to
+    4096 of K, four above; at M <= 8 only above 256 tiles), with as many tiles per
+    workgroup as splits (more above 256 tiles) and at most 2 steps of 256 per wave
+    above M = 8, 4 at M <= 8 (with 4, at most 5 tiles); else unsplit over more
+    tiles than CUs, 2 to 8 tiles per workgroup at M <= 8, 3 to 8 above."""
+    if not 1 <= M <= 32 or (K // 64) % 4 != 0 or N < 16:
+        return None
+    nq, tiles = K // 256, (N + 15) // 16
+    nsmax = 4 if M <= 8 else 2
+    if workspace and tiles <= 512 and nq >= 16 and (M > 8 or tiles > 256):
+        S = 2 if M <= 8 or nq <= 16 else 4
+        it = S if tiles <= 256 else -(-(tiles * S) // 256)
+        ns = -(-(-(-nq // S)) // 8)
+        if ns <= nsmax and it <= 8 and (ns < 4 or it <= 5):
+            return it
+    ns, it = -(-nq // 8), -(-tiles // 256)
+    if (tiles > 256 and 1 <= ns <= nsmax and (2 if M <= 8 else 3) <= it <= 8
+            and (ns < 4 or it <= 5)):
+        return it
+    return None
+
+
 def kernel_label(M, N, K, workspace=True):
     """Name of the kernel a product of this shape runs, by the library's dispatch
     rule (a label for the bench line only): the vector-ALU GEMV for M <= 2 and for
-    M = 3, 4 above 5120 rows (but M = 4 above 16384 rows where the streaming form
-    takes it); with K a multiple of 256, the streaming MFMA form when there are
-    more 16-column tiles than CUs (2 to 8 per CU at M <= 8 with at most 4 steps of
-    256 per wave, 3 to 8 per CU above with at most 2), or, given a workspace, with
-    K split over up to 512 tiles (from 4096 of K; at M <= 8 only above 256 tiles);
-    else quad steps for M <= 8, MFMA pair steps up to M = 32; the prefill tiles
-    beyond."""
-    tiles, steps = (N + 15) // 16, K // 256
-    per_cu = -(-tiles // 256)
-    nsmax = 4 if M <= 8 else 2
-    ns = -(-steps // 8)
-    streams = (M <= 32 and K % 256 == 0 and tiles > 256 and ns <= nsmax
-               and (2 if M <= 8 else 3) <= per_cu <= (5 if ns == 4 else 8))
-    if (workspace and M <= 32 and K % 256 == 0 and N >= 16 and tiles <= 512 and steps >= 16
-            and (M > 8 or tiles > 256)):
-        S = 2 if M <= 8 or steps <= 16 else 4
-        it = S if tiles <= 256 else -(-(tiles * S) // 256)
-        nss = -(-(-(-steps // S)) // 8)
-        streams = streams or (nss <= nsmax and it <= (5 if nss == 4 else 8))
-    if (M <= 2 or (M <= 4 and N > 5120)) and not (M == 4 and N > 16384 and streams):
+    M = 3, 4 above 5120 rows (but M = 4 above 16384 rows where the unsplit
+    streaming form takes it); the streaming MFMA form where it has a plan
+    (`stream_tiles`); else quad steps for M <= 8 with K a multiple of 256, MFMA
+    pair steps up to M = 32; the prefill tiles beyond."""
+    it = stream_tiles(M, N, K, workspace)
+    unsplit = stream_tiles(M, N, K, False)
+    if (M <= 2 or (M <= 4 and N > 5120)) and not (M == 4 and N > 16384 and unsplit):
         return "gemv_valu_kernel"
-    if streams:
+    if it is not None:
         return "gemm_mfma_stream_kernel"
     if M <= 8 and K % 256 == 0:
         return "gemm_mfma_quad_kernel"
@@ -212,13 +225,20 @@ def kernel_label(M, N, K, workspace=True):
     return "gemm_prefill_kernel"
 
 
-def dtype_label(M, shapes):
+def dtype_label(M, shapes, workspace=True):
     """The arithmetic the kernels of this M run: f16 dot products on the vector
-    ALUs, bf16 MFMA with hi + lo level halves, or both within one step."""
+    ALUs, f16 MFMA (the streaming form from 5 tiles per workgroup: activations in
+    f16 under a per-group power-of-two shift), bf16 MFMA with hi + lo level
+    halves (every other MFMA kernel), or several of these within one step."""
     kinds = set()
     for N, K in shapes:
-        k = kernel_label(M, N, K)
-        kinds.add("f16-dot" if k == "gemv_valu_kernel" else "bf16-mfma")
+        k = kernel_label(M, N, K, workspace)
+        if k == "gemv_valu_kernel":
+            kinds.add("f16-dot")
+        elif k == "gemm_mfma_stream_kernel" and stream_tiles(M, N, K, workspace) >= 5:
+            kinds.add("f16-mfma")
+        else:
+            kinds.add("bf16-mfma")
     return "nf4-w/bf16-x/" + "+".join(sorted(kinds)) + "/fp32-acc"
 
 

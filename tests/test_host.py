@@ -108,6 +108,21 @@ def test_stats_and_dtype_labels():
     assert bench.dtype_label(4, [(6144, 4096), (4096, 4096)]) == \
         "nf4-w/bf16-x/bf16-mfma+f16-dot/fp32-acc"
     assert bench.dtype_label(64, [(4096, 4096)]) == "nf4-w/bf16-x/bf16-mfma/fp32-acc"
+    # the 8B launches: f16 MFMA where the streaming form gets 5 or more tiles (gate|up)
+    b8 = [(6144, 4096), (4096, 4096), (28672, 4096), (4096, 14336)]
+    assert bench.dtype_label(8, b8) == "nf4-w/bf16-x/bf16-mfma+f16-mfma/fp32-acc"
+    assert bench.dtype_label(4, b8) == "nf4-w/bf16-x/bf16-mfma+f16-dot+f16-mfma/fp32-acc"
+
+
+@pytest.mark.parametrize("M,N,K,it", [
+    # the stream kernel instances the 8B kernel traces show (<rows, steps, tiles, ...>)
+    (32, 28672, 4096, 7), (32, 6144, 4096, 3), (32, 4096, 4096, 2), (32, 4096, 14336, 4),
+    (4, 28672, 4096, 7), (8, 28672, 4096, 7), (8, 6144, 4096, 3),
+    # no plan: one tile per CU at M <= 8 (quad steps), K not a multiple of 256, M > 32
+    (8, 4096, 4096, None), (8, 4096, 14336, None), (16, 4096, 14464, None),
+    (64, 28672, 4096, None)])
+def test_stream_tiles_follow_the_plan_rule(M, N, K, it):
+    assert bench.stream_tiles(M, N, K) == it
 
 
 def test_build_record_matches_the_sources():
