@@ -220,6 +220,32 @@ def test_prefill_split_matches_oracle_and_repeats(nf4, M, N, K):
     _check(Y0[:, r], Yr, A, f"prefill unsplit M={M} N={N} K={K}")
 
 
+# the 16-byte scale blocks (whole blocks of 8 x KS groups per workgroup, each
+# in-workgroup split a contiguous KS-th of its range): 64 x 64 tiles (KS = 4),
+# 64 x 128 and 128 x 128 (KS = 2), unsplit and with workgroup K-splits
+@pytest.mark.parametrize("M,N,K,ws", [(64, 300, 2048, False), (100, 4096, 4096, True),
+                                      (128, 11520, 1024, False), (256, 11520, 2048, False),
+                                      (512, 4096, 8192, True)])
+def test_prefill_scale_blocks(nf4, M, N, K, ws):
+    W = wl.weights(N, K, 0.02, seed=N + 7 * K + M, device=DEV)
+    X = wl.activations(M, K, seed=3 * N + K + M, device=DEV)
+    codes, scales = _pack(nf4, W)
+    if ws:
+        need = nf4.prefill_workspace_bytes(N, K, M)
+        assert need > 0
+        ws_buf, w = guard.alloc(need, torch.uint8, DEV, fill=0)
+        ws_buf[:guard.GUARD] = guard.SENTINEL
+        ws_buf[guard.GUARD + w.numel():] = guard.SENTINEL
+        Y = _prefill_ws(nf4, codes, scales, X, w, ws_buf)
+    else:
+        Y = _prefill(nf4, codes, scales, X)
+    rows = _rows(N, 64, M + N) if N * K > 2 ** 22 else np.arange(N)
+    r = torch.from_numpy(rows).to(DEV)
+    ref_p, ref_s, _ = oracle.quantize_pack(W[r].cpu().numpy())
+    Yr, A = oracle.gemm(ref_p, ref_s, wl.bf16_bits(X))
+    _check(Y[:, r], Yr, A, f"prefill scale blocks M={M} N={N} K={K} ws={ws}")
+
+
 def test_prefill_split_planned_for_small_grids(nf4):
     assert nf4.prefill_workspace_bytes(4096, 4096, 64) > 0
     assert nf4.prefill_workspace_bytes(300, 2048, 100) > 0
