@@ -116,8 +116,9 @@ __device__ __forceinline__ void for_slots(F &&f, std::integer_sequence<int, d...
 
 }  // namespace
 
-// KS K-splits of 4 waves each: split q takes groups q, q + KS, q + 2 KS, ... of
-// the same output tile, and the splits' tiles are added in split order at the end.
+// KS K-splits of 4 waves each over the same output tile: split q takes groups q,
+// q + KS, q + 2 KS, ... or (SB) the q-th KS-th of the workgroup's groups, and the
+// splits' tiles are added in split order at the end.
 template <int RM, int CN, int P, int KS, bool SB>
 __global__ void __launch_bounds__(kPThreads * KS)
     gemm_prefill_kernel(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
